@@ -1,0 +1,125 @@
+"""The oracle: standard attention, computed in fp64 on the CPU, one (b, h) at a time.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Nothing here is fused,
+tiled or reordered: the three steps are those of standard attention, and the
+method the GPU library implements reaches the same result up to rounding
+order ([FA-1拆解] "核心思想：IO 感知" — exact, not an approximation;
+[15-779 L5] §5.1 "为什么是精确的").
+
+Steps, as the pages give them:
+
+1. S = scale · Q Kᵀ   ([cicada] §1.2 formula and §1.3 steps one and two;
+   [15-779 L5] §2.3).  The scale multiplies S before the max and the exp
+   ([15-779 L5] §5.1 pseudo-code writes S_ij = Q_i K_jᵀ / √d).
+2. Causal mask: S_ij = −∞ where key j lies after query i ([cicada] §1.3 step
+   two; [15-779 L5] §2.3).  Square and top-left aligned: query i sees keys
+   0..i.
+3. Safe softmax per row: m = max_j S_ij, E = exp(S − m), ℓ = Σ_j E,
+   P = E / ℓ ([cicada] §1.3 step three; [15-779 L5] §4.2).
+4. O = P V ([cicada] §1.3 step four) and the per-row log-sum-exp
+   L = m + ln ℓ ([cicada] §3.2.3 "核心计算 2"; [15-779 L5] §5.1 last line).
+
+Decode is the same definition with a single query row that sees every cached
+key ([15-779 L5] §8.1–8.2): no mask and no split — splitting the keys is the
+method's speed device ([15-779 L5] §8.4), not part of the result.
+
+Inputs are whatever the caller hands in (numpy arrays, or torch tensors of any
+dtype, including bfloat16); they are widened to float64 exactly.  ``scale`` is
+used as given (the GPU library receives the same value as an fp32 number,
+which a Python float represents exactly).
+"""
+
+import numpy as np
+
+
+def as_f64(x):
+    """Widen an array-like (numpy array or torch tensor) to a float64 ndarray."""
+    if hasattr(x, "detach"):  # torch tensor: plain CPU conversion, exact for bf16/fp32
+        return x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q, k, scale, causal, rows=None):
+    """Steps 1–2 for one (b, h): S = scale · q kᵀ, then the causal mask.
+
+    q: [R, d] float64 query rows; k: [Nk, d] float64 keys.
+    rows: the query index of each row of ``q`` (defaults to 0..R-1); it places
+    the causal mask, which removes key j from query i when j > i
+    ([cicada] §1.3 step two; [15-779 L5] §2.3).
+    Returns S as a [R, Nk] float64 array with −∞ in masked slots.
+    """
+    s = scale * (q @ k.T)
+    if causal:
+        if rows is None:
+            rows = np.arange(q.shape[0])
+        rows = np.asarray(rows)
+        keys = np.arange(k.shape[0])
+        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def safe_softmax(s):
+    """Step 3: row-wise safe softmax ([15-779 L5] §4.2; [cicada] §1.3 step three).
+
+    Returns (P, m, ℓ): the probabilities, the row maxima and the row sums of
+    exp(S − m).  Masked entries (−∞) get exactly zero weight.
+    """
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    p = e / l[:, None]
+    return p, m, l
+
+
+def attention_ref(q, k, v, scale, causal, rows=None):
+    """Exact attention forward: O = softmax(scale·QKᵀ [+ causal mask]) V and LSE.
+
+    q, k, v: [B, H, N, d] (v may have its own last dimension d_v).
+    rows: optional 1-D array of query indices; only those rows are computed
+    (each output row depends on its own query row only, so a subset is the
+    same definition evaluated at fewer points).
+    Returns (O [B, H, R, d_v], LSE [B, H, R]) as float64 arrays; LSE is the
+    natural-log log-sum-exp of the scaled, masked logits of each row.
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    B, H, N, _ = q.shape
+    if rows is None:
+        rows = np.arange(N)
+    rows = np.asarray(rows)
+    o = np.empty((B, H, rows.size, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, rows.size), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h][rows], k[b, h], scale, causal, rows)
+            p, m, l = safe_softmax(s)
+            o[b, h] = p @ v[b, h]
+            lse[b, h] = m + np.log(l)
+    return o, lse
+
+
+def decode_ref(q, k, v, scale):
+    """Decode: one new query per sequence attends to all Lkv cached keys.
+
+    q: [B, H, d] or [B, H, 1, d]; k, v: [B, H, Lkv, d].  No mask: the new
+    token sees every earlier token ([15-779 L5] §8.1–8.2).  No split.
+    Returns (O [B, H, d], LSE [B, H]) in float64.
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    B, H, _ = q.shape
+    o = np.empty((B, H, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (k[b, h] @ q[b, h])          # [Lkv] logits
+            m = s.max()
+            e = np.exp(s - m)
+            l = e.sum()
+            o[b, h] = (e / l) @ v[b, h]
+            lse[b, h] = m + np.log(l)
+    return o, lse

@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs and the workload table — shared by tests, bench and smoke.
+
+This module holds none of the attention arithmetic: it only draws numbers.
+Both the GPU library's callers and the oracle's callers take their inputs from
+here, so the two sides see the same bytes.
+
+Recipe (every tensor is bf16, i.i.d. N(0, 1)):
+
+* One torch ``Generator`` per (workload, tensor, b, h), seeded with
+  ``seed_for(...)``, so any single head can be regenerated on its own.
+* ``torch.randn`` in float32, then round-to-nearest-even to bfloat16.
+* The Llama-3-8B-shaped workload scales 1 % of the key rows of every (b, h) by
+  8: exactly round(0.01·N) distinct rows, chosen by a seeded permutation,
+  multiplied after the bf16 rounding (×8 is exact in bf16).  These large
+  logits force running-max rescales.
+* Decode K/V (8.6 GB at full size) are drawn on the device that will hold them
+  (the generator runs where the tensor lives); a CPU draw and a GPU draw with
+  the same seed differ, so a GPU test takes the oracle's copy of a head from
+  the device tensor itself.
+"""
+
+from dataclasses import dataclass, replace
+import math
+
+import numpy as np
+import torch
+
+BASE_SEED = 31_2026
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "prefill" or "decode"
+    B: int
+    H: int
+    N: int               # query length (1 for decode)
+    d: int
+    causal: bool = False
+    lkv: int = 0         # decode: cached keys per sequence
+    num_splits: int = 0  # decode: KV splits
+    boost_frac: float = 0.0
+    boost: float = 1.0
+    wid: int = 0         # seed namespace
+
+    @property
+    def scale(self) -> float:
+        """fp32(1/sqrt(d)) as a Python float (the value the library receives)."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads: shapes, distributions and structure of the pages' cases.
+WORKLOADS = [
+    Workload("single_head_b1h1n256d64", "prefill", 1, 1, 256, 64, False, wid=1),
+    Workload("gpt2_small_causal_b8h12n1024d64", "prefill", 8, 12, 1024, 64, True, wid=2),
+    Workload("llama3_8b_causal_b1h32n4096d128_kboost", "prefill", 1, 32, 4096, 128, True,
+             boost_frac=0.01, boost=8.0, wid=3),
+    Workload("long_noncausal_b1h16n16384d128", "prefill", 1, 16, 16384, 128, False, wid=4),
+    Workload("decode_b16h32_lkv32768_d128_s64", "decode", 16, 32, 1, 128, False,
+             lkv=32768, num_splits=64, wid=5),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3}
+
+
+def seed_for(w: Workload, tensor: str, b: int, h: int) -> int:
+    return BASE_SEED + (((w.wid * 8 + _TENSOR_ID[tensor]) * 4096 + b) * 4096 + h)
+
+
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def randn_bf16(seed: int, shape, device="cpu") -> torch.Tensor:
+    """i.i.d. N(0,1) drawn in fp32 with the given seed, rounded to bf16."""
+    g = _gen(seed, device)
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+
+
+def boosted_rows(w: Workload, b: int, h: int, n: int) -> torch.Tensor:
+    """The round(frac·n) distinct key rows of head (b, h) that get scaled."""
+    cnt = int(round(w.boost_frac * n))
+    perm = torch.randperm(n, generator=_gen(seed_for(w, "boost", b, h)))
+    return perm[:cnt]
+
+
+def prefill_head(w: Workload, tensor: str, b: int, h: int, n: int | None = None) -> torch.Tensor:
+    """One [N, d] head of q, k or v (CPU, bf16)."""
+    n = w.N if n is None else n
+    x = randn_bf16(seed_for(w, tensor, b, h), (n, w.d))
+    if tensor == "k" and w.boost_frac > 0.0:
+        x[boosted_rows(w, b, h, n)] *= w.boost
+    return x
+
+
+def make_prefill(w: Workload):
+    """q, k, v as CPU bf16 tensors [B, H, N, d]."""
+    out = []
+    for t in ("q", "k", "v"):
+        x = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16)
+        for b in range(w.B):
+            for h in range(w.H):
+                x[b, h] = prefill_head(w, t, b, h)
+        out.append(x)
+    return tuple(out)
+
+
+def make_decode_q(w: Workload) -> torch.Tensor:
+    """The decode queries [B, H, 1, d] (CPU, bf16)."""
+    q = torch.empty((w.B, w.H, 1, w.d), dtype=torch.bfloat16)
+    for b in range(w.B):
+        for h in range(w.H):
+            q[b, h, 0] = randn_bf16(seed_for(w, "q", b, h), (w.d,))
+    return q
+
+
+def make_decode_kv(w: Workload, device="cpu"):
+    """Decode K, V [B, H, Lkv, d] bf16, drawn on ``device`` head by head."""
+    k = torch.empty((w.B, w.H, w.lkv, w.d), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    for b in range(w.B):
+        for h in range(w.H):
+            k[b, h] = randn_bf16(seed_for(w, "k", b, h), (w.lkv, w.d), device)
+            v[b, h] = randn_bf16(seed_for(w, "v", b, h), (w.lkv, w.d), device)
+    return k, v
+
+
+def prefill_flops(w: Workload) -> float:
+    """4·N²·d·B·H, halved when causal (softmax work is not counted)."""
+    f = 4.0 * w.N * w.N * w.d * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def decode_bytes(w: Workload) -> float:
+    """Algorithmic bytes of one decode call: K and V once, q in, O out (bf16), LSE out (fp32)."""
+    return float(w.B * w.H * (2 * w.lkv * w.d * 2 + 2 * w.d * 2 + 4))
+
+
+def prefill_bytes(w: Workload) -> float:
+    """Algorithmic bytes of one prefill call: Q, K, V in and O out (bf16), LSE out (fp32)."""
+    return float(w.B * w.H * (4 * w.N * w.d * 2 + 4 * w.N))

@@ -1,0 +1,383 @@
+"""Pins for the fp64 oracle: closed forms, brute force, library special cases,
+invariants, and the method's algebra (online = two-pass, ⊕ associativity).
+
+Each test ties the oracle to something other than itself, chosen so that a
+plausible slip (a dropped scale, a wrong mask direction, a transposed operand,
+an LSE without its max) fails at least one of them; ``test_pins_catch_mistakes``
+plants exactly those slips in copies of the oracle and checks that they fail.
+"""
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import attention_ref, decode_ref, safe_softmax, scores
+from oracle.compare import bf16_half_ulp, bf16_rne, check_prefill
+import _method_fp64 as M
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "closed_form_4tok.json")
+
+
+def _fx():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def _frac_mat(rows):
+    return [[Fraction(x) for x in r] for r in rows]
+
+
+def _fixture_inputs(fx):
+    w = np.array([[float(Fraction(x)) for x in r] for r in fx["w"]])
+    q = np.log(w)[None, None]
+    k = (2.0 * np.eye(4))[None, None]
+    v = np.array(fx["v"], dtype=np.float64)[None, None]
+    return q, k, v, float(Fraction(fx["scale"]))
+
+
+# --------------------------------------------------------------------------
+# closed form
+
+
+def test_fixture_is_self_consistent():
+    """P rows are the normalised visible weights and O = P·V, in exact rationals."""
+    fx = _fx()
+    w = _frac_mat(fx["w"])
+    v = [[Fraction(x) for x in r] for r in fx["v"]]
+    p = _frac_mat(fx["causal"]["p"])
+    for i in range(4):
+        tot = sum(w[i][: i + 1])
+        for j in range(4):
+            assert p[i][j] == (w[i][j] / tot if j <= i else 0)
+        assert Fraction(fx["causal"]["lse_ln_of"][i]) == tot
+    for mode in ("causal", "noncausal"):
+        o = _frac_mat(fx[mode]["o"])
+        for i in range(4):
+            vis = range(i + 1) if mode == "causal" else range(4)
+            tot = sum(w[i][j] for j in vis)
+            assert Fraction(fx[mode]["lse_ln_of"][i]) == tot
+            for c in range(4):
+                assert o[i][c] == sum(w[i][j] * v[j][c] for j in vis) / tot
+
+
+@pytest.mark.parametrize("mode", ["causal", "noncausal"])
+def test_oracle_matches_closed_form(mode):
+    fx = _fx()
+    q, k, v, scale = _fixture_inputs(fx)
+    o, lse = attention_ref(q, k, v, scale, causal=(mode == "causal"))
+    want_o = np.array([[float(x) for x in r] for r in _frac_mat(fx[mode]["o"])])
+    want_l = np.array([math.log(int(x)) for x in fx[mode]["lse_ln_of"]])
+    np.testing.assert_allclose(o[0, 0], want_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], want_l, rtol=0, atol=1e-13)
+    if mode == "causal":
+        p, _, _ = safe_softmax(scores(q[0, 0], k[0, 0], scale, True))
+        want_p = np.array([[float(x) for x in r] for r in _frac_mat(fx["causal"]["p"])])
+        np.testing.assert_allclose(p, want_p, rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# 50-digit brute force with the naive definition (valid: nothing overflows)
+
+
+def _decimal_attention(q, k, v, scale, causal):
+    getcontext().prec = 50
+    n, d = q.shape
+    dq = [[Decimal(float(x)) for x in r] for r in q]
+    dk = [[Decimal(float(x)) for x in r] for r in k]
+    dv = [[Decimal(float(x)) for x in r] for r in v]
+    ds = Decimal(scale)
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    for i in range(n):
+        vis = range(i + 1) if causal else range(k.shape[0])
+        e = {j: (ds * sum(dq[i][t] * dk[j][t] for t in range(d))).exp() for j in vis}
+        tot = sum(e.values())
+        for c in range(v.shape[1]):
+            o[i, c] = float(sum(e[j] * dv[j][c] for j in vis) / tot)
+        lse[i] = float(tot.ln())
+    return o, lse
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_oracle_matches_decimal_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 9))
+    d = int(rng.integers(1, 9))
+    causal = bool(seed % 2)
+    q = rng.standard_normal((1, 1, n, d))
+    k = rng.standard_normal((1, 1, n, d))
+    v = rng.standard_normal((1, 1, n, d))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attention_ref(q, k, v, scale, causal)
+    wo, wl = _decimal_attention(q[0, 0], k[0, 0], v[0, 0], scale, causal)
+    np.testing.assert_allclose(o[0, 0], wo, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], wl, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# special cases that reduce to a library routine or a closed form
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_values_give_library_softmax(causal):
+    """With V = I the output rows are the softmax rows themselves."""
+    rng = np.random.default_rng(7)
+    n, d = 11, 5
+    q = rng.standard_normal((1, 1, n, d)) * 2
+    k = rng.standard_normal((1, 1, n, d)) * 2
+    v = np.eye(n)[None, None]
+    scale = 0.37
+    o, lse = attention_ref(q, k, v, scale, causal)
+    logits = scale * (q[0, 0] @ k[0, 0].T)
+    if causal:
+        logits = np.where(np.triu(np.ones((n, n), bool), 1), -np.inf, logits)
+    np.testing.assert_allclose(o[0, 0], scipy.special.softmax(logits, axis=1), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], scipy.special.logsumexp(logits, axis=1), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_running_mean(causal):
+    """K = 0 makes every visible weight equal: O is a (cumulative) mean of V, L = ln(#visible)."""
+    rng = np.random.default_rng(3)
+    n, d = 37, 6
+    q = rng.standard_normal((1, 1, n, d))
+    k = np.zeros((1, 1, n, d))
+    v = rng.standard_normal((1, 1, n, d))
+    o, lse = attention_ref(q, k, v, 0.5, causal)
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    want = np.cumsum(v[0, 0], axis=0) / cnt[:, None] if causal else np.broadcast_to(v[0, 0].mean(0), (n, d))
+    np.testing.assert_allclose(o[0, 0], want, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], np.log(cnt), rtol=0, atol=1e-14)
+
+
+def test_huge_logits_stay_finite_and_exact():
+    """Logits near 1000 overflow the naive exp; the safe softmax gives the closed form."""
+    q = np.array([[[[1000.0, 1000.0 + math.log(3.0)], [5.0, 5.0]]]])
+    k = np.eye(2)[None, None]
+    v = np.array([[[[4.0, -8.0], [0.0, 12.0]]]])
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.exp(q[0, 0, 0]).sum())      # the naive form overflows
+    o, lse = attention_ref(q, k, v, 1.0, causal=False)
+    np.testing.assert_allclose(o[0, 0, 0], [1.0, 7.0], rtol=0, atol=1e-12)   # P = [1/4, 3/4]
+    np.testing.assert_allclose(lse[0, 0, 0], 1000.0 + math.log(4.0), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_invariants(causal):
+    rng = np.random.default_rng(11)
+    n, d = 50, 16
+    q = rng.standard_normal((n, d)) * 3
+    k = rng.standard_normal((n, d)) * 3
+    s = scores(q, k, 0.25, causal)
+    p, m, l = safe_softmax(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p >= 0)
+    if causal:
+        assert np.all(p[np.triu(np.ones((n, n), bool), 1)] == 0.0)   # masked weights are exactly zero
+        assert np.all(np.isneginf(s[np.triu(np.ones((n, n), bool), 1)]))
+
+
+def test_causal_row0_sees_only_key0():
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((2, 3, 9, 4)) for _ in range(3))
+    o, lse = attention_ref(q, k, v, 0.3, causal=True)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.3 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), rtol=0, atol=1e-14)
+
+
+def test_row_subset_equals_full():
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 2, 40, 8)) for _ in range(3))
+    rows = np.array([0, 3, 17, 39])
+    for causal in (False, True):
+        o, lse = attention_ref(q, k, v, 0.5, causal)
+        os_, ls_ = attention_ref(q, k, v, 0.5, causal, rows=rows)
+        np.testing.assert_array_equal(os_, o[:, :, rows])
+        np.testing.assert_array_equal(ls_, lse[:, :, rows])
+
+
+# --------------------------------------------------------------------------
+# the method's algebra against the oracle
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_online_blocked_equals_two_pass(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 200))
+    d = int(rng.choice([4, 16, 64]))
+    causal = bool(seed % 2)
+    br, bc = int(rng.integers(1, 70)), int(rng.integers(1, 70))
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    k[rng.choice(n, size=max(1, n // 20), replace=False)] *= 8.0     # force rescales
+    o, lse = attention_ref(q[None, None], k[None, None], v[None, None], 1 / math.sqrt(d), causal)
+    bo, bl = M.blocked_forward(q, k, v, 1 / math.sqrt(d), causal, br, bc)
+    np.testing.assert_allclose(bo, o[0, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(bl, lse[0, 0], rtol=0, atol=1e-13)
+
+
+def test_merge_is_associative_and_commutative():
+    """Four merge orders over 10 000 numbers all equal logsumexp and the weighted sum."""
+    rng = np.random.default_rng(2024)
+    x = rng.standard_normal(10_000) * 4 + 20
+    v = rng.standard_normal((10_000, 3))
+    want_lse = scipy.special.logsumexp(x)
+    w = np.exp(x - want_lse)
+    want_o = w @ v
+
+    def fold(parts):
+        acc = parts[0]
+        for p in parts[1:]:
+            acc = M.merge_mlo(acc, p)
+        return acc
+
+    def tree(parts):
+        while len(parts) > 1:
+            nxt = [M.merge_mlo(parts[i], parts[i + 1]) for i in range(0, len(parts) - 1, 2)]
+            if len(parts) % 2:
+                nxt.append(parts[-1])
+            parts = nxt
+        return parts[0]
+
+    singles = [M.summary(x[i:i + 1], v[i:i + 1]) for i in range(0, 10_000, 1)]
+    cuts = np.sort(rng.choice(np.arange(1, 10_000), size=6, replace=False))
+    edges = [0, *cuts.tolist(), 10_000]
+    blocks = [M.summary(x[a:b], v[a:b]) for a, b in zip(edges[:-1], edges[1:])]
+    shuffled = [blocks[i] for i in rng.permutation(len(blocks))]
+    for res in (fold(singles), fold(blocks), tree(singles), fold(shuffled)):
+        m, l, o = res
+        assert abs(m + math.log(l) - want_lse) <= 1e-13
+        np.testing.assert_allclose(o / l, want_o, rtol=0, atol=1e-13)
+    # the (m, ℓ) pair alone merges the same way
+    m, l = M.summary(x[:1])
+    for i in range(1, 10_000):
+        m, l = M.merge_ml((m, l), M.summary(x[i:i + 1]))
+    assert abs(m + math.log(l) - want_lse) <= 1e-13
+
+
+def test_rescale_count_statistic():
+    """Max updates over N i.i.d. values average H_N − 1 (7.895 for N = 4096)."""
+    rng = np.random.default_rng(77)
+    n, trials = 4096, 400
+    counts = [M.count_rescales(rng.standard_normal(n)) for _ in range(trials)]
+    h = sum(1.0 / i for i in range(2, n + 1))
+    var = sum((1.0 / i) * (1 - 1.0 / i) for i in range(2, n + 1))
+    assert abs(h - 7.895) < 1e-3
+    assert abs(np.mean(counts) - h) < 5 * math.sqrt(var / trials)
+
+
+# --------------------------------------------------------------------------
+# decode
+
+
+def test_decode_ref_is_the_last_query_row():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 3, 1, 16))
+    k, v = rng.standard_normal((2, 3, 70, 16)), rng.standard_normal((2, 3, 70, 16))
+    o, lse = decode_ref(q, k, v, 0.25)
+    ao, al = attention_ref(q, k, v, 0.25, causal=False)
+    np.testing.assert_allclose(o, ao[:, :, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, al[:, :, 0], rtol=0, atol=1e-14)
+    # the same query placed last in a causal prefill over the same keys sees them all
+    qq = np.concatenate([rng.standard_normal((2, 3, 69, 16)), q], axis=2)
+    co, cl = attention_ref(qq, k, v, 0.25, causal=True, rows=np.array([69]))
+    np.testing.assert_allclose(o, co[:, :, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, cl[:, :, 0], rtol=0, atol=1e-14)
+
+
+def test_decode_single_key():
+    rng = np.random.default_rng(4)
+    q, k, v = rng.standard_normal((1, 2, 8)), rng.standard_normal((1, 2, 1, 8)), rng.standard_normal((1, 2, 1, 8))
+    o, lse = decode_ref(q, k, v, 0.5)
+    np.testing.assert_array_equal(o, v[:, :, 0])
+    np.testing.assert_allclose(lse, 0.5 * np.einsum("bhd,bhd->bh", q, k[:, :, 0]), rtol=0, atol=1e-15)
+
+
+def test_decode_split_merge_equals_decode_ref():
+    """Split the keys into segments, summarise each, ⊕-merge: the unsplit result."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal(32)
+    k, v = rng.standard_normal((1000, 32)), rng.standard_normal((1000, 32))
+    o, lse = decode_ref(q[None, None], k[None, None], v[None, None], 0.2)
+    s = 0.2 * (k @ q)
+    for nsplit in (1, 3, 64, 1000):
+        edges = [(i * 1000) // nsplit for i in range(nsplit + 1)]
+        parts = [M.summary(s[a:b], v[a:b]) for a, b in zip(edges[:-1], edges[1:])]
+        acc = parts[0]
+        for p in parts[1:]:
+            acc = M.merge_mlo(acc, p)
+        np.testing.assert_allclose(acc[2] / acc[1], o[0, 0], rtol=0, atol=1e-13)
+        assert abs(acc[0] + math.log(acc[1]) - lse[0, 0]) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# the tolerance rule
+
+
+def test_bf16_rounding_helpers():
+    assert bf16_half_ulp(4.5) == 2.0 ** -6          # [4, 8): ulp 2^-5
+    assert bf16_half_ulp(3.0) == 2.0 ** -7
+    assert bf16_half_ulp(1.0) == 2.0 ** -8
+    assert bf16_rne(1.0 + 2.0 ** -8) == 1.0          # tie -> even
+    assert bf16_rne(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    x = np.array([0.1, -2.7, 5.3, 100.0])
+    assert np.all(np.abs(bf16_rne(x) - x) <= bf16_half_ulp(x))
+    r = check_prefill(bf16_rne(x), [0.0], x, [0.0005])
+    assert r["pass"] and r["floor"] > 0
+    r = check_prefill(x + 0.02, [0.0], x, [0.0])
+    assert not r["ok"]
+
+
+# --------------------------------------------------------------------------
+# the pins are sensitive: plausible slips planted in copies of the oracle fail them
+
+
+def _mutant(kind):
+    def run(q, k, v, scale, causal):
+        q, k, v = q[0, 0], k[0, 0], v[0, 0]
+        if kind == "no_scale":
+            s = q @ k.T
+        elif kind == "transposed":
+            s = scale * (k @ q.T)
+        else:
+            s = scale * (q @ k.T)
+        if causal:
+            n = s.shape[0]
+            mask = np.tril(np.ones((n, n), bool), -1) if kind == "mask_flipped" else np.triu(np.ones((n, n), bool), 1)
+            s = np.where(mask, -np.inf, s)
+        m = s.max(1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(1)
+        o = (e / l[:, None]) @ v
+        lse = np.log(l) if kind == "lse_no_max" else m + np.log(l)
+        return o[None, None], lse[None, None]
+    return run
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "transposed", "mask_flipped", "lse_no_max"])
+def test_pins_catch_mistakes(kind):
+    fx = _fx()
+    q, k, v, scale = _fixture_inputs(fx)
+    failed = False
+    for mode in ("causal", "noncausal"):
+        o, lse = _mutant(kind)(q, k, v, scale, mode == "causal")
+        want_o = np.array([[float(x) for x in r] for r in _frac_mat(fx[mode]["o"])])
+        want_l = np.array([math.log(int(x)) for x in fx[mode]["lse_ln_of"]])
+        if not (np.allclose(o[0, 0], want_o, atol=1e-9) and np.allclose(lse[0, 0], want_l, atol=1e-9)):
+            failed = True
+    if kind == "lse_no_max":
+        # S = ln w here, so max-free LSE only shows with shifted logits: use the huge-logit case
+        q2 = np.array([[[[1000.0, 1000.0 + math.log(3.0)]]]])
+        k2 = np.eye(2)[None, None]
+        _, l2 = _mutant(kind)(q2, k2, np.ones((1, 1, 2, 1)), 1.0, False)
+        failed = failed or abs(l2[0, 0, 0] - (1000.0 + math.log(4.0))) > 1e-9
+    assert failed
