@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * prefill  fa_fwd    B1 H32 N4096 d128, causal, bf16 (1 % of key rows ×8)
+  * decode   fa_decode B16 H32 Lkv32768 d128, 64 KV splits, bf16
+W untimed warm-up steps, then K timed steps between device synchronisations.
+Each call is also timed with HIP events recorded on the stream it runs on
+(torch's current stream), which gives the per-kernel figures:
+  * value            prefill TFLOP/s = 4·N²·d·B·H / 2 (causal) ÷ fa_fwd time
+  * decode.value     GB/s of algorithmic bytes (K, V once; q in; O, LSE out)
+  * roofline         fa_fwd against the bf16 dense MFMA peak (2.5166 PFLOP/s)
+  * roofline_decode  the decode pair against the HBM peak (8 TB/s)
+  * cpu_baseline     the fp64 oracle on a bounded sample of the same workload,
+                     on this host's cores (rank 0, N=1 only)
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 256 * 4 * 1024 * 2.4e9 / 1e12   # 2516.6: 256 CUs × 4 SIMDs × 1024 FLOP/clk × 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+
+METRIC = "fwd attention TFLOP/s & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "fwd", "decode"], default="all",
+                    help="time one call kind only (for counter collection)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 --pmc (JSON), if present")
+    return ap.parse_args()
+
+
+def cpu_baseline(wf, wd, q, k, v, qd, kd, vd, budget_s):
+    """Time the oracle (as it is) on a bounded sample: whole heads of each workload."""
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, str(threads))
+    import numpy as np
+    from oracle import attention_ref, decode_ref
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(threads)
+        used = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        used = threads
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < wf.H and time.perf_counter() - t0 < budget_s * 0.75:
+        attention_ref(qc[:, heads:heads + 1], kc[:, heads:heads + 1], vc[:, heads:heads + 1], wf.scale, wf.causal)
+        heads += 1
+    t_f = time.perf_counter() - t0
+    flops = 4.0 * wf.N * wf.N * wf.d * heads / (2 if wf.causal else 1)
+    t1 = time.perf_counter()
+    dheads = 0
+    while dheads < wd.B * wd.H and time.perf_counter() - t1 < budget_s * 0.25:
+        b, h = divmod(dheads, wd.H)
+        decode_ref(qd[b:b + 1, h:h + 1].cpu(), kd[b:b + 1, h:h + 1].cpu(), vd[b:b + 1, h:h + 1].cpu(), wd.scale)
+        dheads += 1
+    t_d = time.perf_counter() - t1
+    dbytes = dheads * (2 * wd.lkv * wd.d * 2 + 2 * wd.d * 2 + 4)
+    return {
+        "value": flops / t_f / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": f"{heads} of {wf.H} prefill heads ({wf.name}) in {t_f:.1f} s, fp64 NumPy",
+        "decode": {"value": dbytes / t_d / 1e9, "unit": "GB/s",
+                   "sample": f"{dheads} of {wd.B * wd.H} decode heads ({wd.name}) in {t_d:.1f} s "
+                             "(device-to-host copy of each head included)"},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the single-GPU figure is the measurement.", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_31_amd as fa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wf = synth.BY_NAME["llama3_8b_causal_b1h32n4096d128_kboost"]
+    wd = synth.BY_NAME["decode_b16h32_lkv32768_d128_s64"]
+    print(f"[bench] generating inputs: {wf.name}, {wd.name}", file=sys.stderr, flush=True)
+    q, k, v = (t.to(dev) for t in synth.make_prefill(wf))
+    qd = synth.make_decode_q(wd).to(dev)
+    kd, vd = synth.make_decode_kv(wd, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    do_f = args.only in ("all", "fwd")
+    do_d = args.only in ("all", "decode")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if do_f:
+            fa.fa_fwd(q, k, v, scale=wf.scale, causal=wf.causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        if do_d:
+            fa.fa_decode(qd, kd, vd, scale=wd.scale, num_splits=wd.num_splits, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs] if do_f else []
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs] if do_d else []
+
+    flops = synth.prefill_flops(wf)
+    fbytes = synth.prefill_bytes(wf)
+    dbytes = synth.decode_bytes(wd)
+    f_avg = sum(fwd_ms) / len(fwd_ms) if fwd_ms else None
+    d_avg = sum(dec_ms) / len(dec_ms) if dec_ms else None
+
+    traffic = {}
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic))
+        except Exception:
+            traffic = {}
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (f_avg * 1e-3) / 1e12, 2) if f_avg else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wf.name} + {wd.name}",
+            "prefill": {"B": wf.B, "H": wf.H, "N": wf.N, "d": wf.d, "causal": wf.causal, "scale": wf.scale},
+            "decode": {"B": wd.B, "H": wd.H, "Lkv": wd.lkv, "d": wd.d, "num_splits": wd.num_splits},
+            "parallelism": "single GPU",
+        },
+    }
+    if f_avg:
+        tf = flops / (f_avg * 1e-3) / 1e12
+        out["prefill"] = {"ms": round(f_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tf, 2),
+                          "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        out["roofline"] = {"kernel": "fa_fwd_kernel<128,true>", "bound": "mfma", "achieved": round(tf, 2),
+                           "peak": round(MFMA_BF16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "traffic": traffic.get("fwd"), "algorithmic_bytes": fbytes}
+    if d_avg:
+        gbs = dbytes / (d_avg * 1e-3) / 1e9
+        out["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4), "ms_min": round(min(dec_ms), 4),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        out["roofline_decode"] = {"kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
+                                  "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": traffic.get("decode"), "algorithmic_bytes": dbytes}
+    if not args.no_cpu_baseline and args.only == "all":
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,174 @@
+"""Python binding of the exact-attention HIP library (``libfa.so``).
+
+Argument marshalling only: the functions below check tensors, allocate the
+outputs with torch (device memory and the current stream are all torch is used
+for) and call the C ABI declared in ``include/fa.h``.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback — if the
+library is missing or fails to load, the calls raise.
+
+    fa_fwd(q, k, v, scale=None, causal=False)        -> (o, lse)
+    fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
+    fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
+    fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
+    fa_fwd_tile_shape(d)                             -> (block_m, block_n)
+    fa_status_str(status)                            -> str
+"""
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
+    5: "FA_ERR_VALUE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_LAUNCH", 8: "FA_ERR_ALIAS",
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({fa_status_str(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m exact_attention_31_amd.build` "
+            "(or __graft_entry__.build()) first — there is no non-HIP fallback"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_fwd_tile_pairs.argtypes = [i, i, i]
+    lib.fa_fwd_tile_pairs.restype = ctypes.c_longlong
+    lib.fa_fwd_tile_shape.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.fa_fwd_tile_shape.restype = i
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def fa_fwd_tile_pairs(N: int, d: int, causal: bool) -> int:
+    return int(load_library().fa_fwd_tile_pairs(int(N), int(d), int(bool(causal))))
+
+
+def fa_fwd_tile_shape(d: int):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = load_library().fa_fwd_tile_shape(int(d), ctypes.byref(bm), ctypes.byref(bn))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_tile_shape")
+    return bm.value, bn.value
+
+
+def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(load_library().fa_decode_workspace_bytes(int(B), int(H), int(d), int(num_splits)))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """Prefill: O = softmax(scale·QKᵀ [+ causal mask])·V and LSE, q/k/v bf16 [B, H, N, d].
+
+    Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]).  ``scale`` defaults to
+    fp32(1/sqrt(d)).  Runs asynchronously on the current stream.
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
+    """Split-KV decode: q bf16 [B, H, 1, d], k/v bf16 [B, H, Lkv, d].
+
+    Returns (o bf16 [B, H, 1, d], lse fp32 [B, H]).  ``num_splits`` defaults
+    to enough segments to give ≥ 4 workgroups per compute unit; the workspace
+    is allocated with torch when not given.  Runs on the current stream.
+    """
+    torch = _torch()
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    _check(v, "v", 4)
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence, q has {one}")
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    L = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = max(1, min(L, -(-1024 // (B * H)), max(1, L // 256)))
+    need = fa_decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = load_library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, L, d, float(scale), int(num_splits), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+    return o, lse

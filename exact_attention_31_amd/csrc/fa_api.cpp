@@ -1,0 +1,145 @@
+// C-ABI entry points: argument checks, kernel-instance choice, grid set-up.
+// Every check runs before the first HIP call, so the library can be loaded
+// and its error paths exercised on a host without a GPU.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Element count B·H·N·d with overflow checks; 0 on overflow.
+size_t count4(int B, int H, int N, int d) {
+  const unsigned long long c = (unsigned long long)B * (unsigned long long)H * (unsigned long long)N *
+                               (unsigned long long)d;
+  if (c > (1ull << 46)) return 0;  // far beyond any device memory
+  return (size_t)c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H, N or Lkv < 1, or the sizes overflow";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case FA_ERR_VALUE: return "non-finite scale, or num_splits outside [1, Lkv]";
+    case FA_ERR_WORKSPACE: return "decode workspace missing or smaller than required";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+fa_status fa_fwd_tile_shape(int d, int* block_m, int* block_n) {
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_m) *block_m = fa::kFwdBlockM;
+  if (block_n) *block_n = fa::fwd_block_n(d);
+  return FA_OK;
+}
+
+long long fa_fwd_tile_pairs(int N, int d, int causal) {
+  if (N < 1 || (d != 64 && d != 128)) return -1;
+  const int nq = fa::ceil_div(N, fa::kFwdBlockM);
+  long long pairs = 0;
+  for (int qb = 0; qb < nq; ++qb) pairs += fa::fwd_kv_tiles(N, d, causal, qb);
+  return pairs;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t elems = count4(B, H, N, d);
+  if (elems == 0 || (unsigned long long)B * H > (1ull << 24) ||
+      (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * 4;
+  if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(lse, lb, q, tb) ||
+      overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) || overlap(o, tb, lse, lb))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.BH = B * H;
+  p.N = N;
+  p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
+  const long long total = (long long)p.BH * p.n_qblk;
+  p.xcd_remap = (total % 8 == 0) && ((total / 8) % p.n_qblk == 0);
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  if (fa::launch_fwd(p, d, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || num_splits < 1 || (d != 64 && d != 128)) return 0;
+  const size_t parts = (size_t)B * H * num_splits;
+  const size_t o_bytes = parts * d * 4;                 // a multiple of 256: LSE part stays aligned
+  return o_bytes + parts * 4;
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lkv,
+                    int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Lkv < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t kv_elems = count4(B, H, Lkv, d);
+  if (kv_elems == 0 || (unsigned long long)B * H * num_splits > 0x7fffffffull) return FA_ERR_SHAPE;
+  if (!isfinite(scale) || num_splits < 1 || num_splits > Lkv) return FA_ERR_VALUE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)B * H * d * 2, kb = kv_elems * 2, lb = (size_t)B * H * 4;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) || overlap(lse, lb, q, qb) ||
+      overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(o, qb, lse, lb) ||
+      overlap(workspace, need, q, qb) || overlap(workspace, need, k, kb) || overlap(workspace, need, v, kb) ||
+      overlap(workspace, need, o, qb) || overlap(workspace, need, lse, lb))
+    return FA_ERR_ALIAS;
+
+  fa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)B * H * num_splits * d * 4);
+  p.H = H;
+  p.L = Lkv;
+  p.S = num_splits;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  if (fa::launch_decode(p, B, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+}  // extern "C"

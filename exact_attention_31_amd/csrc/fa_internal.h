@@ -1,0 +1,62 @@
+// Internal declarations shared by the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// Prefill tiling: a workgroup of 4 wavefronts owns 128 query rows (32 per
+// wavefront, split-Q: every row's reductions stay inside one wavefront); key
+// tiles hold 8192 elements, i.e. 64 keys at d = 128 and 128 keys at d = 64.
+constexpr int kFwdWaves = 4;
+constexpr int kFwdThreads = 64 * kFwdWaves;
+constexpr int kFwdBlockM = 32 * kFwdWaves;
+
+__host__ __device__ constexpr int fwd_block_n(int d) { return 8192 / d; }
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Number of key tiles query block `qb` visits.  Causal: only tiles whose first
+// key is not after the block's last query row (tiles wholly above the
+// diagonal are never loaded).
+__host__ __device__ inline int fwd_kv_tiles(int N, int d, int causal, int qb) {
+  const int kv_end = causal ? (N < (qb + 1) * kFwdBlockM ? N : (qb + 1) * kFwdBlockM) : N;
+  return ceil_div(kv_end, fwd_block_n(d));
+}
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int BH;
+  int N;
+  int n_qblk;
+  int xcd_remap;     // 1: group each head's query blocks on one XCD
+  float scale;       // softmax scale (for the LSE)
+  float scale_log2;  // scale · log2(e): logits go straight into exp2
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  float* part_o;     // [BH, S, d] fp32
+  float* part_lse;   // [BH, S]    fp32
+  int H;
+  int L;
+  int S;
+  float scale;
+  float scale_log2;
+};
+
+hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream);
+
+}  // namespace fa

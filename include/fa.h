@@ -1,0 +1,113 @@
+/* fa.h — C ABI of the exact-attention library for MI355X (gfx950).
+ *
+ * Two operations, both exact attention (the result of standard attention up to
+ * rounding order), each returning the output O and the per-row log-sum-exp L:
+ *
+ *   fa_fwd     prefill: O = softmax(scale · Q Kᵀ [+ causal mask]) V, computed as
+ *              one fused, tiled pass with an online softmax, so the N×N score
+ *              and probability matrices never exist in device memory.
+ *              Definition: [cicada] §1.2–1.3 (scaled dot-product attention and
+ *              its steps); the loop order, running (m, ℓ, Õ) state, single
+ *              division and L = m + ln ℓ follow [cicada] §3.2.1–3.2.3 and
+ *              [15-779 L5] §5.1; skipping of key tiles wholly above the
+ *              diagonal follows [15-779 L5] §6.2.
+ *   fa_decode  decode: one new query per sequence against Lkv cached keys, with
+ *              the keys split into segments whose partial results are merged by
+ *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5).
+ *
+ * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
+ * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
+ * 案例：Transformer、注意力与 FlashAttention" (CMU 15-779 lecture 5 notes).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or retains device memory.
+ * - bf16 tensors are raw IEEE bfloat16 (2 bytes), fp32 tensors are IEEE float.
+ * - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *   Calls enqueue work and return without synchronising.
+ * - Every argument check runs before any HIP call; a failed check returns a
+ *   status and enqueues nothing.  A failed launch returns FA_ERR_LAUNCH.  No
+ *   exceptions or aborts cross the ABI.
+ * - Base pointers must be 16-byte aligned (FA_ERR_ALIGN).
+ * - Outputs must not overlap the inputs (FA_ERR_ALIAS).
+ * - Supported head dimensions: d ∈ {64, 128} (FA_ERR_UNSUPPORTED otherwise).
+ * - Thread safety: calls hold no global mutable state and may be issued from
+ *   several host threads; calls on one stream run in stream order.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,       /* B, H, N or Lkv < 1, or the sizes overflow           */
+  FA_ERR_UNSUPPORTED = 3, /* head dimension other than 64 or 128                 */
+  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned               */
+  FA_ERR_VALUE = 5,       /* non-finite scale, or num_splits outside [1, Lkv]    */
+  FA_ERR_WORKSPACE = 6,   /* decode workspace missing or smaller than required   */
+  FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch            */
+  FA_ERR_ALIAS = 8        /* an output overlaps an input                         */
+} fa_status;
+
+/* Prefill forward.
+ *   q, k, v : bf16 [B, H, N, d], contiguous row-major (d fastest).
+ *   o       : bf16 [B, H, N, d], written in full.
+ *   lse     : fp32 [B, H, N], natural-log log-sum-exp of each row's scaled,
+ *             masked logits: L_i = ln Σ_j exp(scale · q_i·k_j).
+ *   scale   : multiplies Q Kᵀ before the softmax (1/sqrt(d) in the usual case).
+ *   causal  : nonzero masks key j from query i when j > i (square, top-left
+ *             aligned: query i sees keys 0..i).
+ * Any N ≥ 1 is accepted; N need not be a multiple of a tile. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa_decode needs for these sizes: the per-split
+ * partial results, fp32 [B, H, num_splits, d] then fp32 [B, H, num_splits].
+ * Returns 0 when the sizes are invalid. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/* Split-KV decode (one query per sequence, no mask).
+ *   q, o    : bf16 [B, H, 1, d].
+ *   k, v    : bf16 [B, H, Lkv, d], contiguous per (b, h) (the cached keys and
+ *             values, read in place: segments are views, not copies).
+ *   lse     : fp32 [B, H].
+ *   num_splits : number of key segments, 1 ≤ num_splits ≤ Lkv.  Segment s
+ *             covers keys [⌊s·Lkv/S⌋, ⌊(s+1)·Lkv/S⌋).
+ *   workspace : device buffer of at least fa_decode_workspace_bytes(...) bytes,
+ *             16-byte aligned, owned by the caller; its contents on entry are
+ *             ignored and on exit are unspecified.  Calls that share one
+ *             workspace must be ordered (same stream), or they race.
+ * Two kernels run in stream order: the per-segment partials, then the ⊕
+ * combine that writes o and lse. */
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Lkv, int d, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of (query block, key tile) pairs fa_fwd processes for one (b, h):
+ * with T tiles per side this is T(T+1)/2 when causal and T² otherwise, the
+ * tiles wholly above the diagonal being skipped ([15-779 L5] §6.2).
+ * Host-only; returns -1 for invalid arguments. */
+long long fa_fwd_tile_pairs(int N, int d, int causal);
+
+/* Query-block and key-tile sizes fa_fwd uses for head dimension d (host-only);
+ * returns FA_ERR_UNSUPPORTED for other d. */
+fa_status fa_fwd_tile_shape(int d, int* block_m, int* block_n);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_str(int status);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,130 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/fa.h declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_31_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("libfa.so not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+                 "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert set(_declared()) <= exported
+
+
+def test_status_strings_and_version():
+    _lib()
+    assert fa.fa_abi_version() == 1
+    assert fa.fa_status_str(0) == "ok"
+    for s in range(1, 9):
+        assert fa.fa_status_str(s) not in ("ok", "unknown status")
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+# fake, 16-byte aligned, distinct "device" addresses: every call below must be
+# rejected by validation, so nothing ever dereferences them
+P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(6)]
+MISALIGNED = ctypes.c_void_p(0x10000008)
+
+
+def _fwd(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, scale=0.125, causal=0):
+    return _lib().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), causal, None)
+
+
+def _dec(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, L=16, d=64, scale=0.125, S=4, ws=P[5], wsb=1 << 20):
+    return _lib().fa_decode(q, k, v, o, lse, B, H, L, d, ctypes.c_float(scale), S, ws, wsb, None)
+
+
+def test_fwd_argument_checks():
+    assert _fwd(q=None) == 1
+    assert _fwd(lse=None) == 1
+    assert _fwd(B=0) == 2 and _fwd(H=-1) == 2 and _fwd(N=0) == 2
+    assert _fwd(d=96) == 3 and _fwd(d=256) == 3
+    assert _fwd(scale=float("nan")) == 5 and _fwd(scale=float("inf")) == 5
+    assert _fwd(o=MISALIGNED) == 4
+    assert _fwd(o=P[0]) == 8            # output on top of q
+    assert _fwd(lse=ctypes.c_void_p(0x10000000 + 16)) == 8   # LSE inside q's range
+    assert _fwd(B=1 << 20, H=1 << 20, N=1 << 20) == 2        # sizes overflow
+
+
+def test_decode_argument_checks():
+    assert _dec(k=None) == 1
+    assert _dec(L=0) == 2
+    assert _dec(d=32) == 3
+    assert _dec(S=0) == 5 and _dec(S=17) == 5 and _dec(scale=float("nan")) == 5
+    assert _dec(ws=None) == 6
+    need = _lib().fa_decode_workspace_bytes(1, 1, 64, 4)
+    assert need == 4 * 64 * 4 + 4 * 4
+    assert _dec(wsb=need - 1) == 6
+    assert _dec(v=MISALIGNED) == 4
+    assert _dec(ws=P[0]) == 8            # workspace on top of q
+    assert _lib().fa_decode_workspace_bytes(0, 1, 64, 4) == 0
+    assert _lib().fa_decode_workspace_bytes(1, 1, 80, 4) == 0
+
+
+def test_tile_shape():
+    _lib()
+    assert fa.fa_fwd_tile_shape(128) == (128, 64)
+    assert fa.fa_fwd_tile_shape(64) == (128, 128)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_tile_shape(80)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_tile_skip_counts(d):
+    """Square tiles: T(T+1)/2 of T² (query block, key tile) pairs are visited ([15-779 L5] §6.2)."""
+    _lib()
+    bm, bn = fa.fa_fwd_tile_shape(d)
+    for n in (1, 100, 128, 1000, 4096, 16384):
+        tq = -(-n // bm)
+        tk = -(-n // bn)
+        assert fa.fa_fwd_tile_pairs(n, d, False) == tq * tk
+        # causal: query block i visits the key tiles up to its last row
+        want = sum(-(-min(n, (i + 1) * bm) // bn) for i in range(tq))
+        assert fa.fa_fwd_tile_pairs(n, d, True) == want
+    if bm == bn:
+        for t in (1, 4, 32):
+            assert fa.fa_fwd_tile_pairs(t * bm, d, True) == t * (t + 1) // 2
+    # the page's numbers: T = 4 visits 10 of 16 pairs; at T = 32 the ratio is 51.6 %
+    assert 4 * 5 // 2 == 10 and abs(32 * 33 / 2 / 32 ** 2 - 0.516) < 5e-4
+    assert fa.fa_fwd_tile_pairs(0, d, True) == -1
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    _lib()
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):          # CPU tensors are refused before any call
+        fa.fa_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(q.float(), q, q)

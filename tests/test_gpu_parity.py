@@ -1,0 +1,243 @@
+"""GPU parity: the HIP library, called through the C ABI, against the fp64 oracle
+on the same seeded inputs.
+
+Rule (oracle/compare.py): |O − O_ref| ≤ 1e-2 + ½·ulp_bf16(O_ref) per element
+and |LSE − LSE_ref| ≤ 1e-3, with the literal max-abs error reported beside.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import exact_attention_31_amd as fa
+import synth
+from oracle import attention_ref, decode_ref, check_prefill
+from oracle.compare import bf16_half_ulp
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    fa.load_library()  # raise loudly if the HIP library is missing
+    yield
+
+
+def _run_fwd(q, k, v, scale, causal):
+    o, lse = fa.fa_fwd(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(name, o, lse, ro, rl):
+    rep = check_prefill(o, lse, ro, rl)
+    _say(f"[parity] {name}: O max_abs={rep['max_abs']:.3g} floor={rep['floor']:.3g} "
+         f"excess={rep['excess']:.3g} LSE max_abs={rep['lse_max_abs']:.3g} pass={rep['pass']}")
+    assert rep["pass"], rep
+    return rep
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+
+
+def test_single_head_n256_d64():
+    w = W[0]
+    _say("[case] workload", w.name)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    ro, rl = attention_ref(q, k, v, w.scale, w.causal)
+    _check(w.name, o, lse, ro, rl)
+
+
+def test_gpt2_small_causal():
+    w = W[1]
+    _say("[case] workload", w.name)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    ro, rl = attention_ref(q, k, v, w.scale, w.causal)
+    _check(w.name, o, lse, ro, rl)
+
+
+def test_llama3_causal_kboost():
+    """All 32 heads, every row (the large-logit rows force running-max rescales)."""
+    w = W[2]
+    _say("[case] workload", w.name)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    ro, rl = attention_ref(q, k, v, w.scale, w.causal)
+    _check(w.name, o, lse, ro, rl)
+
+
+def test_long_noncausal_sampled_rows():
+    """N = 16384: the oracle evaluates sampled query rows (first, last, random) of 4 heads."""
+    w = W[3]
+    _say("[case] workload", w.name)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1], rng.choice(w.N, 250, replace=False)]))
+    heads = [0, 5, 10, 15]
+    ro, rl = attention_ref(q[:, heads], k[:, heads], v[:, heads], w.scale, False, rows=rows)
+    _check(w.name + " (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
+
+
+def test_decode_full_size_sampled_heads():
+    """B16 H32 Lkv 32768 d128, 64 splits; the oracle recomputes 8 heads unsplit."""
+    w = W[4]
+    _say("[case] workload", w.name)
+    q = synth.make_decode_q(w).cuda()
+    k, v = synth.make_decode_kv(w, device="cuda")
+    o, lse = fa.fa_decode(q, k, v, scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[:, :, 0]
+    lse = lse.cpu().numpy()
+    picks = [(0, 0), (3, 7), (7, 31), (8, 16), (11, 2), (12, 30), (15, 0), (15, 31)]
+    for b, h in picks:
+        ro, rl = decode_ref(q[b:b + 1, h:h + 1].cpu(), k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.scale)
+        _check(f"{w.name} b{b} h{h}", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
+
+
+# ----------------------------------------------------------------------------
+# ragged and odd shapes, both head dims, both mask modes
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 63, 65, 129, 200, 1000])
+def test_tails(n, causal, d):
+    w = W[1].with_(B=2, H=3, N=n, d=d, causal=causal, wid=40 + d)
+    _say(f"[case] tails n={n} causal={causal} d={d}")
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, causal)
+    ro, rl = attention_ref(q, k, v, w.scale, causal)
+    _check(f"tails n={n} causal={causal} d={d}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_tail_past_xcd_remap(d):
+    """N = 4097 (one row past a tile) with B·H·blocks divisible by 8 and not."""
+    for B, H in ((1, 8), (1, 3)):
+        w = W[2].with_(B=B, H=H, N=4097, d=d, boost_frac=0.0, wid=60 + d + H)
+        _say(f"[case] n=4097 B={B} H={H} d={d}")
+        q, k, v = synth.make_prefill(w)
+        for causal in (False, True):
+            o, lse = _run_fwd(q, k, v, w.scale, causal)
+            rows = np.array([0, 1, 2, 127, 128, 2048, 4095, 4096])
+            ro, rl = attention_ref(q, k, v, w.scale, causal, rows=rows)
+            _check(f"n=4097 B={B} H={H} d={d} causal={causal}", o[:, :, rows], lse[:, :, rows], ro, rl)
+
+
+# ----------------------------------------------------------------------------
+# special cases
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_row0_is_v0(d):
+    w = W[1].with_(B=1, H=4, N=300, d=d, causal=True, wid=70 + d)
+    q, k, v = synth.make_prefill(w)
+    o, lse = fa.fa_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])          # weight exactly 1 on key 0
+    want = w.scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1)
+    assert torch.allclose(lse[:, :, 0].cpu().double(), want, atol=1e-4, rtol=0)
+
+
+def test_large_logits_are_stable():
+    """Inputs ×16 (logits in the hundreds): finite outputs within the rule."""
+    w = W[2].with_(B=1, H=2, N=700, wid=80)
+    q, k, v = synth.make_prefill(w)
+    q = q * 16
+    for causal in (False, True):
+        o, lse = _run_fwd(q, k, v, w.scale, causal)
+        ro, rl = attention_ref(q, k, v, w.scale, causal)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        _check(f"large logits causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_split_extremes(d):
+    """num_splits = 1, = Lkv (one key each), uneven, and the default."""
+    w = W[4].with_(B=2, H=3, lkv=1000, d=d, wid=90 + d)
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w)
+    ro, rl = decode_ref(q, k, v, w.scale)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for s in (1, 3, 7, 64, 999, 1000, None):
+        o, lse = fa.fa_decode(qd, kd, vd, scale=w.scale, num_splits=s)
+        torch.cuda.synchronize()
+        _check(f"decode d={d} L=1000 splits={s}", o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("lkv", [1, 2, 17, 4099])
+def test_decode_short_and_ragged(lkv):
+    w = W[4].with_(B=1, H=5, lkv=lkv, wid=100)
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w)
+    ro, rl = decode_ref(q, k, v, w.scale)
+    o, lse = fa.fa_decode(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, num_splits=min(lkv, 8))
+    torch.cuda.synchronize()
+    _check(f"decode L={lkv}", o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), ro, rl)
+    if lkv == 1:
+        assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+# ----------------------------------------------------------------------------
+# every output element written, nothing outside written, determinism
+
+
+def test_canaries_and_guard_bands():
+    w = W[1].with_(B=2, H=2, N=333, d=128, causal=True, wid=110)
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    n_o = q.numel()
+    guard = 4096
+    obuf = torch.full((n_o + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((w.B * w.H * w.N + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    o = obuf[guard:guard + n_o].view(q.shape)
+    lse = lbuf[guard:guard + w.B * w.H * w.N].view(w.B, w.H, w.N)
+    fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert torch.isnan(obuf[:guard]).all() and torch.isnan(obuf[guard + n_o:]).all()
+    assert torch.isnan(lbuf[:guard]).all() and torch.isnan(lbuf[-guard:]).all()
+
+
+def test_deterministic():
+    w = W[2].with_(H=4, N=1500, wid=120)
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    o1, l1 = fa.fa_fwd(q, k, v, scale=w.scale, causal=True)
+    o2, l2 = fa.fa_fwd(q, k, v, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    wd = W[4].with_(B=2, H=4, lkv=5000, wid=121)
+    qd = synth.make_decode_q(wd).cuda()
+    kd, vd = synth.make_decode_kv(wd, device="cuda")
+    a = fa.fa_decode(qd, kd, vd, num_splits=16)
+    b = fa.fa_decode(qd, kd, vd, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_runs_on_a_side_stream():
+    w = W[0]
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    ref_o, ref_l = fa.fa_fwd(q, k, v, scale=w.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = fa.fa_fwd(q, k, v, scale=w.scale)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
