@@ -36,8 +36,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode"], default="all",
-                    help="time one call kind only (for counter collection)")
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "copy"], default="all",
+                    help="time one call kind only (for counter collection); 'copy' times a plain "
+                         "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -86,6 +87,26 @@ def cpu_baseline(wf, wd, q, k, v, qd, kd, vd, budget_s):
     }
 
 
+def copy_reference(torch, dev, args):
+    """A plain device copy of known size: 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -104,19 +125,25 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.only == "copy":
+        return copy_reference(torch, dev, args)
+
     wf = synth.BY_NAME["llama3_8b_causal_b1h32n4096d128_kboost"]
     wd = synth.BY_NAME["decode_b16h32_lkv32768_d128_s64"]
-    print(f"[bench] generating inputs: {wf.name}, {wd.name}", file=sys.stderr, flush=True)
-    q, k, v = (t.to(dev) for t in synth.make_prefill(wf))
-    qd = synth.make_decode_q(wd).to(dev)
-    kd, vd = synth.make_decode_kv(wd, device=dev)
-    ws = torch.empty(fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits), dtype=torch.uint8, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
     do_f = args.only in ("all", "fwd")
     do_d = args.only in ("all", "decode")
+    print(f"[bench] generating inputs: {wf.name}, {wd.name}", file=sys.stderr, flush=True)
+    q = k = v = o = lse = qd = kd = vd = ws = None
+    if do_f or args.only == "all":
+        q, k, v = (t.to(dev) for t in synth.make_prefill(wf))
+        o = torch.empty_like(q)
+        lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device=dev)
+    if do_d:
+        qd = synth.make_decode_q(wd).to(dev)
+        kd, vd = synth.make_decode_kv(wd, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits), dtype=torch.uint8,
+                         device=dev)
+    torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:

@@ -41,7 +41,7 @@ const char* fa_status_str(int s) {
     case FA_ERR_SHAPE: return "B, H, N or Lkv < 1, or the sizes overflow";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
     case FA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
-    case FA_ERR_VALUE: return "non-finite scale, or num_splits outside [1, Lkv]";
+    case FA_ERR_VALUE: return "scale not positive and finite, or num_splits outside [1, Lkv]";
     case FA_ERR_WORKSPACE: return "decode workspace missing or smaller than required";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIAS: return "an output overlaps an input";
@@ -75,7 +75,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (elems == 0 || (unsigned long long)B * H > (1ull << 24) ||
       (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
     return FA_ERR_SHAPE;
-  if (!isfinite(scale)) return FA_ERR_VALUE;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   const size_t tb = elems * 2, lb = (size_t)B * H * N * 4;
   if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(lse, lb, q, tb) ||
@@ -113,7 +113,7 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const size_t kv_elems = count4(B, H, Lkv, d);
   if (kv_elems == 0 || (unsigned long long)B * H * num_splits > 0x7fffffffull) return FA_ERR_SHAPE;
-  if (!isfinite(scale) || num_splits < 1 || num_splits > Lkv) return FA_ERR_VALUE;
+  if (!isfinite(scale) || !(scale > 0.f) || num_splits < 1 || num_splits > Lkv) return FA_ERR_VALUE;
   const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))

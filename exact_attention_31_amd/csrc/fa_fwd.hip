@@ -4,19 +4,28 @@
 // independent, so the grid runs over (b, h, query block) — the loop order
 // with the query block outside and the key/value tiles inside ([cicada]
 // §3.2.1–3.2.2; [15-779 L5] §5.1 and §6.3 "parallel over sequence length").
-// Per key tile j the workgroup:
+// Per key tile j of 64 keys the workgroup:
 //   1. streams K_j, V_j from HBM into LDS (double-buffered: tile j+1 is in
 //      flight in registers while tile j is computed),
 //   2. computes Sᵀ = K_j Q_iᵀ on bf16 MFMA with fp32 accumulation,
 //   3. masks keys after the query on tiles that cross the diagonal and keys
 //      past N on the ragged last tile ([15-779 L5] §6.2),
-//   4. updates the running max m, running sum ℓ and rescales the output
-//      accumulator by exp(m_old − m_new) ([cicada] §3.2.2 steps B–D;
+//   4. keeps the running max m, the running sum ℓ and the output accumulator
+//      consistent with each other — when m grows, ℓ and the accumulator are
+//      multiplied by exp(m_old − m_new) ([cicada] §3.2.2 steps B–D;
 //      [15-779 L5] §4.3–4.5),
 //   5. accumulates Oᵀ += V_jᵀ P̃ᵀ on bf16 MFMA,
 // and after the last tile divides once by ℓ and writes O and
 // L = m + ln ℓ ([cicada] §3.2.3).  Key tiles wholly above the diagonal are
 // never visited ([15-779 L5] §6.2).
+//
+// The reference max m is only moved when some row of the wavefront sees a
+// logit more than kRescaleLog2 (in log2 units) above it; otherwise the stale m
+// is kept for exponent and sum alike, which changes nothing in exact
+// arithmetic (m cancels between ℓ and the accumulator) and bounds every P̃
+// by 2^kRescaleLog2.  This is the conditional rescaling of [cicada] §5
+// (FlashAttention-4), and it removes the accumulator multiply from almost
+// every tile.
 //
 // Pages cited: [cicada] "已有的几种大模型上下文支持情况"; [15-779 L5] "第 5 讲 ·
 // 案例：Transformer、注意力与 FlashAttention".
@@ -25,15 +34,15 @@
 // * The products are taken transposed — Sᵀ = K Qᵀ and Oᵀ = Vᵀ P̃ᵀ — so that
 //   with v_mfma_f32_32x32x16_bf16 each lane's accumulator column is one query
 //   row: the row max and row sum are in-lane plus one exchange between the two
-//   32-lane halves, the rescale factor is a per-lane scalar, and the fp32
-//   scores of Sᵀ are already laid out as the B operand of the second product
-//   (converted to bf16 in place, no LDS round trip).
-// * K tile in LDS: row-major [key][d], 16-byte chunks XOR-swizzled by
-//   (row & 7) so that MFMA operand reads and the staging writes hit distinct
-//   banks.
-// * V tile in LDS: transposed to [d][key] while staging (the reduction index
-//   of Vᵀ P̃ᵀ is the key), stored in 4-key groups of 8 bytes whose group
-//   index is XOR-swizzled by (d + d/16) & 15.
+//   32-lane halves (v_permlane32_swap), the rescale factor is a per-lane
+//   scalar, and the fp32 scores of Sᵀ are already laid out as the B operand of
+//   the second product (converted to bf16 in place, no LDS round trip).
+// * K tile in LDS: row-major [key][d], rows padded to 2d+16 bytes so the MFMA
+//   operand reads (16 rows × 16 bytes per pass) hit distinct banks.
+// * V tile in LDS: row-major [key][d], rows padded to 2d+64 bytes; the Vᵀ
+//   operand, whose reduction index is the key, is read with the LDS transpose
+//   load ds_read_b64_tr_b16, four keys per 16-lane group.
+// * All per-lane LDS addresses are a lane base plus compile-time offsets.
 // * exp is computed as exp2 with scale·log2(e) folded into the logits.
 
 #include <hip/hip_runtime.h>
@@ -46,89 +55,54 @@ namespace fa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// log2-domain growth of the running max that forces a rescale.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Tile {
-  static constexpr int BN = fwd_block_n(D);     // keys per tile
-  static constexpr int CHUNKS = D / 8;          // 16-byte chunks per K/V row
-  static constexpr int ROWS_PER_PASS = kFwdThreads / CHUNKS;
-  static constexpr int K_PASSES = BN / ROWS_PER_PASS;  // 16-byte K loads per thread
-  static constexpr int NSUB = BN / 32;          // 32-key sub-tiles of Sᵀ
-  static constexpr int KS_QK = D / 16;          // MFMA k-steps of Sᵀ = K Qᵀ
-  static constexpr int DSUB = D / 32;           // 32-row sub-tiles of Oᵀ
-  static constexpr int KS_PV = BN / 16;         // MFMA k-steps of Oᵀ += Vᵀ P̃ᵀ
-  static constexpr int K_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * K_BYTES;  // K tile + Vᵀ tile
-  static_assert(K_PASSES == 4, "staging assumes four 16-byte K loads per thread");
-  static_assert(kFwdThreads / CHUNKS * 4 == BN, "staging assumes 4 V rows per thread");
+  static constexpr int BN = fwd_block_n(D);       // keys per tile
+  static constexpr int CH = D / 8;                // 16-byte chunks per K/V row
+  static constexpr int RPP = kFwdThreads / CH;    // rows staged per pass
+  static constexpr int LOADS = BN / RPP;          // 16-byte loads of K (and of V) per thread
+  static constexpr int KS = 2 * D + 16;           // LDS row stride of K (bytes)
+  static constexpr int VS = 2 * D + 64;           // LDS row stride of V (bytes)
+  static constexpr int K_BYTES = BN * KS;
+  static constexpr int STAGE = K_BYTES + BN * VS;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int NSUB = BN / 32;            // 32-key sub-tiles of Sᵀ
+  static constexpr int KS_QK = D / 16;            // MFMA k-steps of Sᵀ = K Qᵀ
+  static constexpr int DSUB = D / 32;             // 32-row sub-tiles of Oᵀ
+  static constexpr int KS_PV = BN / 16;           // MFMA k-steps of Oᵀ += Vᵀ P̃ᵀ
+  static_assert(LOADS * RPP == BN, "staging covers the tile");
 };
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
-
-__device__ inline int k_off(int row, int chunk, int D) {
-  return (row * D + ((chunk ^ (row & 7)) << 3)) * 2;  // bytes within the K tile
+// Both halves of the wavefront end up with f(x_lo, x_hi) for the lane pair (l, l^32).
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-template <int BN>
-__device__ inline int vt_off(int d, int grp) {
-  return (d * BN + ((grp ^ ((d + (d >> 4)) & 15)) << 2)) * 2;  // bytes within the Vᵀ tile
-}
-
-template <int D>
-__device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
-                                 int kv0, int N, int tid, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
-  using T = Tile<D>;
-  const int c = tid % T::CHUNKS;
-  const int r0 = tid / T::CHUNKS;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = kv0 + r0 + i * T::ROWS_PER_PASS;
-    kr[i] = key < N ? *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + c * 8) : u32x4_t{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = kv0 + 4 * r0 + i;
-    vr[i] = key < N ? *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + c * 8) : u32x4_t{0, 0, 0, 0};
-  }
-}
-
-template <int D>
-__device__ inline void store_tile(unsigned char* stage, int tid, const u32x4_t (&kr)[4], const u32x4_t (&vr)[4]) {
-  using T = Tile<D>;
-  const int c = tid % T::CHUNKS;
-  const int r0 = tid / T::CHUNKS;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = r0 + i * T::ROWS_PER_PASS;
-    *reinterpret_cast<u32x4_t*>(stage + k_off(row, c, D)) = kr[i];
-  }
-  // Transpose 4 keys × 8 dims into 8 dims × 4 keys: for dim 8c+e the 8-byte
-  // group holds (v[key0][e], v[key1][e], v[key2][e], v[key3][e]).
-  unsigned char* vt = stage + T::K_BYTES;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    uint32_t lo, hi;
-    if (e & 1) {
-      lo = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-      hi = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-    } else {
-      lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-      hi = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-    }
-    *reinterpret_cast<u32x2_t*>(vt + vt_off<T::BN>(8 * c + e, r0)) = u32x2_t{lo, hi};
-  }
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t r;
   r[0] = (__bf16)a;
   r[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline u32x2_t lds_tr_read(const unsigned char* base, int off) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + off));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // Work index -> (bh, query block).  Workgroups are dealt round-robin to the
@@ -155,7 +129,7 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE_BYTES];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   int bh, qb;
   decode_work(p, bh, qb);
@@ -169,8 +143,18 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   const int wq0 = q0 + wave * 32;  // first query row of this wavefront
   const int q_row = wq0 + i32;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* __restrict__ kbase = p.k + base;
-  const uint16_t* __restrict__ vbase = p.v + base;
+
+  // staging role: 16-byte chunk `sc` of rows sr, sr + RPP, ...
+  const int sc = tid % T::CH;
+  const int sr = tid / T::CH;
+  const uint16_t* __restrict__ kg = p.k + base + (size_t)sr * D + sc * 8;
+  const uint16_t* __restrict__ vg = p.v + base + (size_t)sr * D + sc * 8;
+  const int k_st = sr * T::KS + sc * 16;
+  const int v_st = T::K_BYTES + sr * T::VS + sc * 16;
+  // operand-read lane bases (bytes within a stage)
+  const int k_rd = i32 * T::KS + g * 16;
+  const int jj = lane & 15;
+  const int v_rd = T::K_BYTES + (4 * g + (jj >> 2)) * T::VS + (16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
 
   // Q fragments: the B operand of Sᵀ = K Qᵀ (lane: query q_row, dims 16kk + 8g .. +7).
   bf16x8_t qf[T::KS_QK];
@@ -186,104 +170,139 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
   const float c = p.scale_log2;
 
-  float m = -INFINITY;  // running max of the raw logits q·k (this lane's query row)
-  float l = 0.f;        // running Σ exp2((s - m)·c) over this lane's half of the keys
+  float m = -INFINITY;  // reference max of the raw logits q·k (this lane's query row)
+  // Two running sums over this lane's half of the keys: ℓ of the fp32 P̃ (for
+  // L: rows with few keys need it within 1e-3) and ℓ_b of the bf16-rounded P̃
+  // that enter the MFMA (for O: numerator and denominator then use the same
+  // weights, so a row dominated by one key returns that key's value exactly).
+  float l = 0.f, lb = 0.f;
   f32x16_t acc[T::DSUB];
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
 
-  u32x4_t kr[4], vr[4];
-  load_tile<D>(kbase, vbase, 0, N, tid, kr, vr);
-  store_tile<D>(smem, tid, kr, vr);
+  u32x4_t kr[T::LOADS], vr[T::LOADS];
+  auto load_tile = [&](int kv0) {
+    const size_t off = (size_t)kv0 * D;
+    if (kv0 + T::BN <= N) {
+#pragma unroll
+      for (int i = 0; i < T::LOADS; ++i) {
+        kr[i] = *reinterpret_cast<const u32x4_t*>(kg + off + (size_t)i * T::RPP * D);
+        vr[i] = *reinterpret_cast<const u32x4_t*>(vg + off + (size_t)i * T::RPP * D);
+      }
+    } else {  // ragged last tile: rows past N are zero (their logits are masked)
+#pragma unroll
+      for (int i = 0; i < T::LOADS; ++i) {
+        const bool in = kv0 + sr + i * T::RPP < N;
+        kr[i] = in ? *reinterpret_cast<const u32x4_t*>(kg + off + (size_t)i * T::RPP * D) : u32x4_t{0, 0, 0, 0};
+        vr[i] = in ? *reinterpret_cast<const u32x4_t*>(vg + off + (size_t)i * T::RPP * D) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](unsigned char* stage) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      *reinterpret_cast<u32x4_t*>(stage + k_st + i * T::RPP * T::KS) = kr[i];
+      *reinterpret_cast<u32x4_t*>(stage + v_st + i * T::RPP * T::VS) = vr[i];
+    }
+  };
+
+  load_tile(0);
+  store_tile(smem);
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int kv0 = j * T::BN;
     const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile<D>(kbase, vbase, kv0 + T::BN, N, tid, kr, vr);
+    if (has_next) load_tile(kv0 + T::BN);
 
-    unsigned char* st_k = smem + (j & 1) * T::STAGE_BYTES;
-    unsigned char* st_v = st_k + T::K_BYTES;
+    const unsigned char* st = smem + (j & 1) * T::STAGE;
     const bool active = !CAUSAL || kv0 <= wq0 + 31;  // else every key of the tile is after every row
     if (active) {
-      // ---- Sᵀ = K Qᵀ -------------------------------------------------------
+      // ---- Sᵀ = K Qᵀ -------------------------------------------------------------
       f32x16_t s[T::NSUB];
 #pragma unroll
-      for (int st = 0; st < T::NSUB; ++st) {
-        s[st] = f32x16_t{};
-        const int row = st * 32 + i32;
+      for (int sub = 0; sub < T::NSUB; ++sub) {
+        u32x4_t kf[T::KS_QK];
 #pragma unroll
-        for (int kk = 0; kk < T::KS_QK; ++kk) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st_k + k_off(row, 2 * kk + g, D));
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[kk], s[st], 0, 0, 0);
-        }
+        for (int kk = 0; kk < T::KS_QK; ++kk)
+          kf[kk] = *reinterpret_cast<const u32x4_t*>(st + k_rd + sub * 32 * T::KS + kk * 32);
+        s[sub] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < T::KS_QK; ++kk)
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], s[sub], 0, 0, 0);
       }
-      // ---- mask: keys after the query (diagonal tiles), keys past N (last tile)
-      const bool need_mask = (kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0);
-      if (need_mask) {
+      // ---- mask: keys after the query (diagonal tiles), keys past N (last tile) --
+      if ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0)) {
         const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 #pragma unroll
-        for (int st = 0; st < T::NSUB; ++st)
+        for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + st * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            if (key > lim) s[st][r] = -INFINITY;
+            const int key = kv0 + sub * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+            if (key > lim) s[sub][r] = -INFINITY;
           }
       }
-      // ---- online softmax -----------------------------------------------------
+      // ---- online softmax -------------------------------------------------------
       float mt = -INFINITY;
 #pragma unroll
-      for (int st = 0; st < T::NSUB; ++st)
+      for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[st][r]);
-      mt = fmaxf(mt, xor32(mt));
-      // The first tile holds key 0, visible to every row, so m is finite from
-      // then on and m_new never is -inf.
-      const float m_new = fmaxf(m, mt);
-      const float mc = m_new * c;
-      const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
-      float rs = 0.f;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
+      mt = pair_max(mt);
+      // The first tile holds key 0, visible to every row: m is finite after it.
+      if (__any((mt - m) * c > kRescaleLog2)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+        l *= alpha;
+        lb *= alpha;
 #pragma unroll
-      for (int st = 0; st < T::NSUB; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[st][r], c, -mc));
-          s[st][r] = e;
-          rs += e;
-        }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
+        for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
+        m = m_new;
+      }
+      const float mc = m * c;
 
-      // ---- Oᵀ += Vᵀ P̃ᵀ ---------------------------------------------------------
+      // ---- P̃ = exp2(s·c − m·c) → bf16; ℓ += Σ P̃; Oᵀ += Vᵀ P̃ᵀ ----------------------
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float rs = 0.f, rsb = 0.f;
 #pragma unroll
       for (int kk = 0; kk < T::KS_PV; ++kk) {
-        const f32x16_t& src = s[kk >> 1];
         const int h8 = (kk & 1) * 8;
         u32x4_t pw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(src[h8 + 2 * e], src[h8 + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
+          rs += e0 + e1;
+          // The pair goes to dot2 directly: fed from an element of the packed
+          // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
+          bf16x2_t pe;
+          pe[0] = (__bf16)e0;
+          pe[1] = (__bf16)e1;
+          rsb = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb, false);
+          pw[e] = __builtin_bit_cast(uint32_t, pe);
+        }
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
         for (int ds = 0; ds < T::DSUB; ++ds) {
-          const int d = ds * 32 + i32;
-          const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(st_v + vt_off<T::BN>(d, 4 * kk + g));
-          const u32x2_t a1 = *reinterpret_cast<const u32x2_t*>(st_v + vt_off<T::BN>(d, 4 * kk + 2 + g));
+          const u32x2_t a0 = lds_tr_read(st, v_rd + 16 * kk * T::VS + ds * 64);
+          const u32x2_t a1 = lds_tr_read(st, v_rd + (16 * kk + 8) * T::VS + ds * 64);
           const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
           acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[ds], 0, 0, 0);
         }
       }
+      l += rs;
+      lb += rsb;
     }
 
-    if (has_next) store_tile<D>(smem + ((j + 1) & 1) * T::STAGE_BYTES, tid, kr, vr);
+    if (has_next) store_tile(smem + ((j + 1) & 1) * T::STAGE);
     __syncthreads();
   }
 
   // ---- epilogue: one division, one store of O and L ------------------------------
-  l += xor32(l);
+  l = pair_sum(l);
+  lb = pair_sum(lb);
   if (q_row < N) {
-    const float inv = 1.f / l;
+    const float inv = 1.f / lb;
     uint16_t* orow = p.o + base + (size_t)q_row * D;
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds)
@@ -301,8 +320,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+  using T = Tile<D>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const dim3 grid(p.BH * p.n_qblk);
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), T::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

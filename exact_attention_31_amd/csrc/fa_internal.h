@@ -10,12 +10,12 @@ namespace fa {
 
 // Prefill tiling: a workgroup of 4 wavefronts owns 128 query rows (32 per
 // wavefront, split-Q: every row's reductions stay inside one wavefront); key
-// tiles hold 8192 elements, i.e. 64 keys at d = 128 and 128 keys at d = 64.
+// tiles hold 64 keys.
 constexpr int kFwdWaves = 4;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBlockM = 32 * kFwdWaves;
 
-__host__ __device__ constexpr int fwd_block_n(int d) { return 8192 / d; }
+__host__ __device__ constexpr int fwd_block_n(int) { return 64; }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

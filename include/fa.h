@@ -50,7 +50,7 @@ typedef enum fa_status {
   FA_ERR_SHAPE = 2,       /* B, H, N or Lkv < 1, or the sizes overflow           */
   FA_ERR_UNSUPPORTED = 3, /* head dimension other than 64 or 128                 */
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned               */
-  FA_ERR_VALUE = 5,       /* non-finite scale, or num_splits outside [1, Lkv]    */
+  FA_ERR_VALUE = 5,       /* scale not > 0 and finite, or num_splits outside [1, Lkv] */
   FA_ERR_WORKSPACE = 6,   /* decode workspace missing or smaller than required   */
   FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch            */
   FA_ERR_ALIAS = 8        /* an output overlaps an input                         */
@@ -61,7 +61,8 @@ typedef enum fa_status {
  *   o       : bf16 [B, H, N, d], written in full.
  *   lse     : fp32 [B, H, N], natural-log log-sum-exp of each row's scaled,
  *             masked logits: L_i = ln Σ_j exp(scale · q_i·k_j).
- *   scale   : multiplies Q Kᵀ before the softmax (1/sqrt(d) in the usual case).
+ *   scale   : multiplies Q Kᵀ before the softmax (1/sqrt(d) in the usual case);
+ *             must be positive and finite (FA_ERR_VALUE otherwise).
  *   causal  : nonzero masks key j from query i when j > i (square, top-left
  *             aligned: query i sees keys 0..i).
  * Any N ≥ 1 is accepted; N need not be a multiple of a tile. */
@@ -78,6 +79,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *   k, v    : bf16 [B, H, Lkv, d], contiguous per (b, h) (the cached keys and
  *             values, read in place: segments are views, not copies).
  *   lse     : fp32 [B, H].
+ *   scale   : as for fa_fwd (positive and finite).
  *   num_splits : number of key segments, 1 ≤ num_splits ≤ Lkv.  Segment s
  *             covers keys [⌊s·Lkv/S⌋, ⌊(s+1)·Lkv/S⌋).
  *   workspace : device buffer of at least fa_decode_workspace_bytes(...) bytes,

@@ -71,6 +71,7 @@ def test_fwd_argument_checks():
     assert _fwd(B=0) == 2 and _fwd(H=-1) == 2 and _fwd(N=0) == 2
     assert _fwd(d=96) == 3 and _fwd(d=256) == 3
     assert _fwd(scale=float("nan")) == 5 and _fwd(scale=float("inf")) == 5
+    assert _fwd(scale=0.0) == 5 and _fwd(scale=-0.125) == 5
     assert _fwd(o=MISALIGNED) == 4
     assert _fwd(o=P[0]) == 8            # output on top of q
     assert _fwd(lse=ctypes.c_void_p(0x10000000 + 16)) == 8   # LSE inside q's range
@@ -81,7 +82,7 @@ def test_decode_argument_checks():
     assert _dec(k=None) == 1
     assert _dec(L=0) == 2
     assert _dec(d=32) == 3
-    assert _dec(S=0) == 5 and _dec(S=17) == 5 and _dec(scale=float("nan")) == 5
+    assert _dec(S=0) == 5 and _dec(S=17) == 5 and _dec(scale=float("nan")) == 5 and _dec(scale=-1.0) == 5
     assert _dec(ws=None) == 6
     need = _lib().fa_decode_workspace_bytes(1, 1, 64, 4)
     assert need == 4 * 64 * 4 + 4 * 4
@@ -95,7 +96,7 @@ def test_decode_argument_checks():
 def test_tile_shape():
     _lib()
     assert fa.fa_fwd_tile_shape(128) == (128, 64)
-    assert fa.fa_fwd_tile_shape(64) == (128, 128)
+    assert fa.fa_fwd_tile_shape(64) == (128, 64)
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile_shape(80)
 
