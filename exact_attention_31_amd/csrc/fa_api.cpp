@@ -72,7 +72,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const size_t elems = count4(B, H, N, d);
-  if (elems == 0 || (unsigned long long)B * H > (1ull << 24) ||
+  // one head's K (and V) is addressed through a buffer descriptor of N·d·2 bytes
+  if (elems == 0 || (unsigned long long)N * d * 2 > 0x7fffffffull || (unsigned long long)B * H > (1ull << 24) ||
       (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
     return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;

@@ -49,6 +49,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -69,18 +71,18 @@ template <int D>
 struct Tile {
   static constexpr int BN = fwd_block_n(D);       // keys per tile
   static constexpr int CH = D / 8;                // 16-byte chunks per K/V row
-  static constexpr int RPP = kFwdThreads / CH;    // rows staged per pass
-  static constexpr int LOADS = BN / RPP;          // 16-byte loads of K (and of V) per thread
-  static constexpr int KS = 2 * D + 16;           // LDS row stride of K (bytes)
-  static constexpr int VS = 2 * D + 64;           // LDS row stride of V (bytes)
-  static constexpr int K_BYTES = BN * KS;
-  static constexpr int STAGE = K_BYTES + BN * VS;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int ROW = 2 * D;               // bytes per K/V row in LDS (unpadded)
+  static constexpr int TILE_BYTES = BN * ROW;     // one K or V tile
+  static constexpr int LOADS = TILE_BYTES / (16 * kFwdThreads);  // 16-byte direct loads per thread per tile
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K0, K1, V0, V1
   static constexpr int NSUB = BN / 32;            // 32-key sub-tiles of Sᵀ
   static constexpr int KS_QK = D / 16;            // MFMA k-steps of Sᵀ = K Qᵀ
   static constexpr int DSUB = D / 32;             // 32-row sub-tiles of Oᵀ
   static constexpr int KS_PV = BN / 16;           // MFMA k-steps of Oᵀ += Vᵀ P̃ᵀ
-  static_assert(LOADS * RPP == BN, "staging covers the tile");
+  static_assert(LOADS * 16 * kFwdThreads == TILE_BYTES, "direct loads cover the tile");
+  // XOR swizzles of the 16-byte chunk index within a row (see the file header).
+  __device__ static int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // Both halves of the wavefront end up with f(x_lo, x_hi) for the lane pair (l, l^32).
@@ -103,6 +105,20 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 __device__ inline u32x2_t lds_tr_read(const unsigned char* base, int off) {
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + off));
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
+// lane L's bytes [voff + soff, +16) land at lds + 16·L (lds uniform across the
+// wavefront); bytes past the buffer's num_records read as zero.  Kept in a
+// non-template function: used directly inside the kernel template, the
+// builtin makes the host pass drop the kernel's launch stub.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Raw buffer descriptor over `bytes` bytes at `base` (word 3: 32-bit data, no swizzle).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
 // Work index -> (bh, query block).  Workgroups are dealt round-robin to the
@@ -130,6 +146,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* const kbuf[2] = {smem, smem + T::TILE_BYTES};
+  unsigned char* const vbuf[2] = {smem + 2 * T::TILE_BYTES, smem + 3 * T::TILE_BYTES};
 
   int bh, qb;
   decode_work(p, bh, qb);
@@ -139,22 +157,44 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   const int wave = tid >> 6;
   const int i32 = lane & 31;  // query column of Sᵀ / Oᵀ owned by this lane
   const int g = lane >> 5;    // which 32-lane half
+  const int jj = lane & 15;
   const int q0 = qb * kFwdBlockM;
   const int wq0 = q0 + wave * 32;  // first query row of this wavefront
   const int q_row = wq0 + i32;
   const size_t base = (size_t)bh * N * D;
 
-  // staging role: 16-byte chunk `sc` of rows sr, sr + RPP, ...
-  const int sc = tid % T::CH;
-  const int sr = tid / T::CH;
-  const uint16_t* __restrict__ kg = p.k + base + (size_t)sr * D + sc * 8;
-  const uint16_t* __restrict__ vg = p.v + base + (size_t)sr * D + sc * 8;
-  const int k_st = sr * T::KS + sc * 16;
-  const int v_st = T::K_BYTES + sr * T::VS + sc * 16;
-  // operand-read lane bases (bytes within a stage)
-  const int k_rd = i32 * T::KS + g * 16;
-  const int jj = lane & 15;
-  const int v_rd = T::K_BYTES + (4 * g + (jj >> 2)) * T::VS + (16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
+  // Direct global->LDS loads: wavefront `wave`, load i fills LDS chunk slots
+  // (i*4 + wave)*64 + lane of the tile; the slot's (row, swizzled chunk) names
+  // the global chunk this lane fetches.  Load i covers rows r0 + i*RPL, and
+  // both swizzles repeat with that period, so load i is load 0 shifted by
+  // i*RPL rows.
+  constexpr int RPL = kFwdWaves * 64 / T::CH;  // rows covered by one load across the workgroup
+  const int r0 = (wave * 64 + lane) / T::CH;
+  const int cpos = lane % T::CH;
+  const int k_goff = r0 * T::ROW + ((cpos ^ T::k_swz(r0)) << 4);
+  const int v_goff = r0 * T::ROW + ((cpos ^ T::v_swz(r0)) << 4);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
+  // rows past N lie past the head's bytes and read as zero (their logits are masked)
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
+  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int goff, int kv0, unsigned char* dst) {
+    unsigned char* d = dst + wave_u * 1024;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) load_lds16(rsrc, d + i * kFwdWaves * 1024, goff, (kv0 + i * RPL) * T::ROW);
+  };
+
+  // Operand-read lane offsets (bytes within a tile).
+  int k_rd[T::KS_QK];  // Kᵀ rows i32 (+32 per sub-tile), chunk 2kk + g
+#pragma unroll
+  for (int kk = 0; kk < T::KS_QK; ++kk) k_rd[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::k_swz(i32)) << 4);
+  int v_rd[T::DSUB];   // transpose reads: rows 4g + jj/4 (+16kk, +8), dims 32ds + 16(G&1) + 4(jj&3)
+  {
+    const int r = 4 * g + (jj >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds)
+      v_rd[ds] = r * T::ROW + (((4 * ds + cl) ^ T::v_swz(r)) << 4) + 8 * (jj & 1);
+  }
 
   // Q fragments: the B operand of Sᵀ = K Qᵀ (lane: query q_row, dims 16kk + 8g .. +7).
   bf16x8_t qf[T::KS_QK];
@@ -169,6 +209,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
 
   const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
   const float c = p.scale_log2;
+  auto active = [&](int j) { return !CAUSAL || j * T::BN <= wq0 + 31; };  // some row of the wave sees the tile
 
   float m = -INFINITY;  // reference max of the raw logits q·k (this lane's query row)
   // Two running sums over this lane's half of the keys: ℓ of the fp32 P̃ (for
@@ -180,122 +221,168 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
 
-  u32x4_t kr[T::LOADS], vr[T::LOADS];
-  auto load_tile = [&](int kv0) {
-    const size_t off = (size_t)kv0 * D;
-    if (kv0 + T::BN <= N) {
+  // ---- Sᵀ = K Qᵀ for one tile (the two 32-key sub-tiles interleaved) ----------------
+  auto qk = [&](const unsigned char* kb, f32x16_t (&s)[T::NSUB]) {
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
-        kr[i] = *reinterpret_cast<const u32x4_t*>(kg + off + (size_t)i * T::RPP * D);
-        vr[i] = *reinterpret_cast<const u32x4_t*>(vg + off + (size_t)i * T::RPP * D);
-      }
-    } else {  // ragged last tile: rows past N are zero (their logits are masked)
+    for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
-        const bool in = kv0 + sr + i * T::RPP < N;
-        kr[i] = in ? *reinterpret_cast<const u32x4_t*>(kg + off + (size_t)i * T::RPP * D) : u32x4_t{0, 0, 0, 0};
-        vr[i] = in ? *reinterpret_cast<const u32x4_t*>(vg + off + (size_t)i * T::RPP * D) : u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](unsigned char* stage) {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      *reinterpret_cast<u32x4_t*>(stage + k_st + i * T::RPP * T::KS) = kr[i];
-      *reinterpret_cast<u32x4_t*>(stage + v_st + i * T::RPP * T::VS) = vr[i];
-    }
-  };
-
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kv0 = j * T::BN;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + T::BN);
-
-    const unsigned char* st = smem + (j & 1) * T::STAGE;
-    const bool active = !CAUSAL || kv0 <= wq0 + 31;  // else every key of the tile is after every row
-    if (active) {
-      // ---- Sᵀ = K Qᵀ -------------------------------------------------------------
-      f32x16_t s[T::NSUB];
+    for (int kk = 0; kk < T::KS_QK; ++kk)
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub) {
-        u32x4_t kf[T::KS_QK];
-#pragma unroll
-        for (int kk = 0; kk < T::KS_QK; ++kk)
-          kf[kk] = *reinterpret_cast<const u32x4_t*>(st + k_rd + sub * 32 * T::KS + kk * 32);
-        s[sub] = f32x16_t{};
-#pragma unroll
-        for (int kk = 0; kk < T::KS_QK; ++kk)
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], s[sub], 0, 0, 0);
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + k_rd[kk] + sub * 32 * T::ROW);
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], s[sub], 0, 0, 0);
       }
-      // ---- mask: keys after the query (diagonal tiles), keys past N (last tile) --
-      if ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0)) {
-        const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
-#pragma unroll
-        for (int sub = 0; sub < T::NSUB; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + sub * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            if (key > lim) s[sub][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax -------------------------------------------------------
-      float mt = -INFINITY;
+  };
+
+  // ---- mask of one tile's scores: keys after the query (diagonal tiles), keys
+  //      past N (last tile); only tiles at the end of the key range need it
+  auto mask = [&](int j, f32x16_t (&s)[T::NSUB]) {
+    const int kv0 = j * T::BN;
+    if ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0)) {
+      const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
-      mt = pair_max(mt);
-      // The first tile holds key 0, visible to every row: m is finite after it.
-      if (__any((mt - m) * c > kRescaleLog2)) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-        l *= alpha;
-        lb *= alpha;
-#pragma unroll
-        for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
-        m = m_new;
-      }
-      const float mc = m * c;
-
-      // ---- P̃ = exp2(s·c − m·c) → bf16; ℓ += Σ P̃; Oᵀ += Vᵀ P̃ᵀ ----------------------
-      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float rs = 0.f, rsb = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < T::KS_PV; ++kk) {
-        const int h8 = (kk & 1) * 8;
-        u32x4_t pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
-          rs += e0 + e1;
-          // The pair goes to dot2 directly: fed from an element of the packed
-          // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
-          bf16x2_t pe;
-          pe[0] = (__bf16)e0;
-          pe[1] = (__bf16)e1;
-          rsb = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb, false);
-          pw[e] = __builtin_bit_cast(uint32_t, pe);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + sub * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          if (key > lim) s[sub][r] = -INFINITY;
         }
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-        for (int ds = 0; ds < T::DSUB; ++ds) {
-          const u32x2_t a0 = lds_tr_read(st, v_rd + 16 * kk * T::VS + ds * 64);
-          const u32x2_t a1 = lds_tr_read(st, v_rd + (16 * kk + 8) * T::VS + ds * 64);
-          const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-          acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[ds], 0, 0, 0);
-        }
-      }
-      l += rs;
-      lb += rsb;
     }
+  };
+  // ---- row max of one tile's scores ------------------------------------------------------
+  auto rowmax = [&](const f32x16_t (&s)[T::NSUB]) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < T::NSUB; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
+    return pair_max(mt);
+  };
+  // ---- move the reference max when some row outgrew it by 2^kRescaleLog2 ----------------
+  auto rescale = [&](float mt) {
+    // The first tile holds key 0, visible to every row: m is finite after it.
+    if (__any((mt - m) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      l *= alpha;
+      lb *= alpha;
+#pragma unroll
+      for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
+      m = m_new;
+    }
+  };
 
-    if (has_next) store_tile(smem + ((j + 1) & 1) * T::STAGE);
+  // ---- P̃ = exp2(s·c − m·c) as packed bf16, and the two row sums -------------------------
+  auto exps = [&](const f32x16_t (&s)[T::NSUB], u32x4_t (&pw)[T::KS_PV]) {
+    const float mc = m * c;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs = 0.f, rsb = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < T::KS_PV; ++kk) {
+      const int h8 = (kk & 1) * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
+        rs += e0 + e1;
+        // The pair goes to dot2 directly: fed from an element of the packed
+        // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
+        bf16x2_t pe;
+        pe[0] = (__bf16)e0;
+        pe[1] = (__bf16)e1;
+        rsb = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb, false);
+        pw[kk][e] = __builtin_bit_cast(uint32_t, pe);
+      }
+    }
+    l += rs;
+    lb += rsb;
+  };
+
+  // ---- Oᵀ += Vᵀ P̃ᵀ ----------------------------------------------------------------------
+  auto pv = [&](const unsigned char* vb, const u32x4_t (&pw)[T::KS_PV]) {
+#pragma unroll
+    for (int kk = 0; kk < T::KS_PV; ++kk)
+#pragma unroll
+      for (int ds = 0; ds < T::DSUB; ++ds) {
+        const u32x2_t a0 = lds_tr_read(vb, v_rd[ds] + 16 * kk * T::ROW);
+        const u32x2_t a1 = lds_tr_read(vb, v_rd[ds] + (16 * kk + 8) * T::ROW);
+        const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+        acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, pw[kk]), acc[ds], 0, 0, 0);
+      }
+  };
+
+  // ---- pipeline: K runs two tiles ahead of the softmax, V one tile ahead -------------
+  // Iteration j reads K_{j+1} (kbuf[(j+1)&1]) and V_j (vbuf[j&1]) and fills
+  // K_{j+2} -> kbuf[j&1], V_{j+1} -> vbuf[(j+1)&1]: every buffer written in
+  // iteration j was last read before the barrier that ended iteration j-1.
+  // Within an iteration the MFMAs of Sᵀ_{j+1} are issued between the exp2 /
+  // convert / sum instructions of tile j, so the matrix and vector units run
+  // side by side; the row max of Sᵀ_{j+1} is taken while Oᵀ += Vᵀ_j P̃ᵀ_j runs.
+  f32x16_t s0[T::NSUB], s1[T::NSUB];
+  load_tile(krsrc, k_goff, 0, kbuf[0]);
+  load_tile(vrsrc, v_goff, 0, vbuf[0]);
+  if (n_tiles > 1) load_tile(krsrc, k_goff, T::BN, kbuf[1]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (active(0)) {
+    qk(kbuf[0], s0);
+    mask(0, s0);
+    rescale(rowmax(s0));
+  }
+  __syncthreads();  // every wave is done with kbuf[0] before K_2 lands in it
+
+  // Tiles 0 .. n_clean-1 need no mask for any row of the workgroup (and, when
+  // causal, are seen by every wavefront); iterations whose next tile is clean
+  // run without mask or activity tests.
+  const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+
+  // kmine/vmine: the buffers this iteration fills (K_{j+2}, V_{j+1});
+  // kread/vread: the ones it reads (K_{j+1}, V_j).  Called with the two
+  // orders alternately, so every buffer address is a constant after inlining.
+  auto iteration = [&](int j, unsigned char* kmine, const unsigned char* kread, unsigned char* vmine,
+                       const unsigned char* vread, f32x16_t(&scur)[T::NSUB], f32x16_t(&snext)[T::NSUB],
+                       auto generic) {
+    constexpr bool GENERIC = decltype(generic)::value;
+    if (j + 2 < n_tiles) load_tile(krsrc, k_goff, (j + 2) * T::BN, kmine);
+    if (j + 1 < n_tiles) load_tile(vrsrc, v_goff, (j + 1) * T::BN, vmine);
+    const bool next = GENERIC ? (j + 1 < n_tiles && active(j + 1)) : true;
+    const bool cur = GENERIC ? active(j) : true;
+    if (cur) {
+      u32x4_t pw[T::KS_PV];
+      if (next) {
+        qk(kread, snext);
+        exps(scur, pw);
+        // issue order: K-fragment reads run two MFMAs ahead; each MFMA of
+        // Sᵀ_{j+1} is followed by six VALU instructions of tile j's softmax
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < T::KS_QK * T::NSUB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        exps(scur, pw);
+      }
+      pv(vread, pw);
+    }
+    // (a wavefront that sees no key of tile j sees none of tile j+1 either)
+    if (cur && next) {
+      if (GENERIC) mask(j + 1, snext);
+      rescale(rowmax(snext));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 < n_clean; j += 2) {
+    iteration(j, kbuf[0], kbuf[1], vbuf[1], vbuf[0], s0, s1, std::false_type{});
+    iteration(j + 1, kbuf[1], kbuf[0], vbuf[0], vbuf[1], s1, s0, std::false_type{});
+  }
+  for (; j < n_tiles; j += 2) {
+    iteration(j, kbuf[0], kbuf[1], vbuf[1], vbuf[0], s0, s1, std::true_type{});
+    if (j + 1 < n_tiles) iteration(j + 1, kbuf[1], kbuf[0], vbuf[0], vbuf[1], s1, s0, std::true_type{});
   }
 
   // ---- epilogue: one division, one store of O and L ------------------------------
