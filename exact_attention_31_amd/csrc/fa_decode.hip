@@ -178,23 +178,61 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodePara
 }
 
 // O = Σ_s w_s O_s / Σ_s w_s and LSE = M + ln Σ_s w_s with w_s = exp(LSE_s − M),
-// M = max_s LSE_s: the ⊕ merge written on normalised partials.
+// M = max_s LSE_s: the ⊕ merge written on normalised partials.  One
+// workgroup per (b, h): the max over segments is a block reduction, then
+// groups of threads take interleaved segments (16-byte loads of O_s, d/4
+// threads per segment) and the groups' partial sums meet in LDS.
+constexpr int kCombThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void fa_decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombThreads) void fa_decode_combine_kernel(DecodeParams p) {
+  constexpr int C4 = D / 4;                    // float4 chunks per partial row
+  constexpr int G = kCombThreads / C4;         // segment groups
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ float red[kCombThreads / 64];
+  __shared__ f32x4_t part[G][C4];
+  __shared__ float wsum[G];
+
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const float* __restrict__ pl = p.part_lse + (size_t)bh * p.S;
-  const float* __restrict__ po = p.part_o + (size_t)bh * p.S * D + d;
-  float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, pl[s]);
-  float W = 0.f, o = 0.f;
-  for (int s = 0; s < p.S; ++s) {
+  const f32x4_t* __restrict__ po = reinterpret_cast<const f32x4_t*>(p.part_o + (size_t)bh * p.S * D);
+
+  float mx = -INFINITY;
+  for (int s = t; s < p.S; s += kCombThreads) mx = fmaxf(mx, pl[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombThreads / 64; ++w) M = fmaxf(M, red[w]);
+
+  const int c = t % C4, gi = t / C4;
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  for (int s = gi; s < p.S; s += G) {
     const float w = __builtin_amdgcn_exp2f((pl[s] - M) * 1.4426950408889634f);
     W += w;
-    o = fmaf(w, po[(size_t)s * D], o);
+    o += w * po[(size_t)s * C4 + c];
   }
-  p.o[(size_t)bh * D + d] = to_bf16(o / W);
-  if (d == 0) p.lse[bh] = M + __builtin_amdgcn_logf(W) * 0.69314718055994531f;
+  part[gi][c] = o;
+  if (c == 0) wsum[gi] = W;
+  __syncthreads();
+  if (t < C4) {
+    f32x4_t sum = part[0][t];
+    float Wt = wsum[0];
+#pragma unroll
+    for (int q = 1; q < G; ++q) {
+      sum += part[q][t];
+      Wt += wsum[q];
+    }
+    const float inv = 1.f / Wt;
+    uint32_t w0 = (uint32_t)to_bf16(sum[0] * inv) | ((uint32_t)to_bf16(sum[1] * inv) << 16);
+    uint32_t w1 = (uint32_t)to_bf16(sum[2] * inv) | ((uint32_t)to_bf16(sum[3] * inv) << 16);
+    *reinterpret_cast<u32x2_t*>(p.o + (size_t)bh * D + 4 * t) = u32x2_t{w0, w1};
+    if (t == 0) p.lse[bh] = M + __builtin_amdgcn_logf(Wt) * 0.69314718055994531f;
+  }
 }
 
 template <int D>
@@ -203,7 +241,7 @@ hipError_t launch_decode_t(const DecodeParams& p, int B, hipStream_t stream) {
   hipLaunchKernelGGL(fa_decode_split_kernel<D>, dim3(BH * p.S), dim3(kDecThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fa_decode_combine_kernel<D>, dim3(BH), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL(fa_decode_combine_kernel<D>, dim3(BH), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();
 }
 

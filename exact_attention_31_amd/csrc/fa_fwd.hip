@@ -74,7 +74,6 @@ struct Tile {
   static constexpr int ROW = 2 * D;               // bytes per K/V row in LDS (unpadded)
   static constexpr int TILE_BYTES = BN * ROW;     // one K or V tile
   static constexpr int LOADS = TILE_BYTES / (16 * kFwdThreads);  // 16-byte direct loads per thread per tile
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K0, K1, V0, V1
   static constexpr int NSUB = BN / 32;            // 32-key sub-tiles of Sᵀ
   static constexpr int KS_QK = D / 16;            // MFMA k-steps of Sᵀ = K Qᵀ
   static constexpr int DSUB = D / 32;             // 32-row sub-tiles of Oᵀ
@@ -145,9 +144,13 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* const kbuf[2] = {smem, smem + T::TILE_BYTES};
-  unsigned char* const vbuf[2] = {smem + 2 * T::TILE_BYTES, smem + 3 * T::TILE_BYTES};
+  // Four separate LDS objects: with distinct objects the compiler can tell
+  // that the direct loads filling one buffer never alias reads of another,
+  // and does not hold those reads back until the loads complete.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES];
+  unsigned char* const kbuf[2] = {k_lds0, k_lds1};
+  unsigned char* const vbuf[2] = {v_lds0, v_lds1};
 
   int bh, qb;
   decode_work(p, bh, qb);
@@ -408,11 +411,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   using T = Tile<D>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
   const dim3 grid(p.BH * p.n_qblk);
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), T::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@ here, so the two sides see the same bytes.
 
 Recipe (every tensor is bf16, i.i.d. N(0, 1)):
 
-* One torch ``Generator`` per (workload, tensor, b, h), seeded with
+* Prefill q, k, v and decode q: one torch ``Generator`` per (workload, tensor, b, h), seeded with
   ``seed_for(...)``, so any single head can be regenerated on its own.
 * ``torch.randn`` in float32, then round-to-nearest-even to bfloat16.
 * The Llama-3-8B-shaped workload scales 1 % of the key rows of every (b, h) by
@@ -14,7 +14,8 @@ Recipe (every tensor is bf16, i.i.d. N(0, 1)):
   multiplied after the bf16 rounding (×8 is exact in bf16).  These large
   logits force running-max rescales.
 * Decode K/V (8.6 GB at full size) are drawn on the device that will hold them
-  (the generator runs where the tensor lives); a CPU draw and a GPU draw with
+  (the generator runs where the tensor lives), one generator per (workload,
+  tensor, sequence b) covering all heads of b; a CPU draw and a GPU draw with
   the same seed differ, so a GPU test takes the oracle's copy of a head from
   the device tensor itself.
 """
@@ -121,13 +122,12 @@ def make_decode_q(w: Workload) -> torch.Tensor:
 
 
 def make_decode_kv(w: Workload, device="cpu"):
-    """Decode K, V [B, H, Lkv, d] bf16, drawn on ``device`` head by head."""
+    """Decode K, V [B, H, Lkv, d] bf16, drawn on ``device`` one sequence (all heads) at a time."""
     k = torch.empty((w.B, w.H, w.lkv, w.d), dtype=torch.bfloat16, device=device)
     v = torch.empty_like(k)
     for b in range(w.B):
-        for h in range(w.H):
-            k[b, h] = randn_bf16(seed_for(w, "k", b, h), (w.lkv, w.d), device)
-            v[b, h] = randn_bf16(seed_for(w, "v", b, h), (w.lkv, w.d), device)
+        k[b] = randn_bf16(seed_for(w, "k", b, 0), (w.H, w.lkv, w.d), device)
+        v[b] = randn_bf16(seed_for(w, "v", b, 0), (w.H, w.lkv, w.d), device)
     return k, v
 
 
