@@ -40,14 +40,91 @@ def parse():
                     help="time one call kind only (for counter collection); 'copy' times a plain "
                          "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 --pmc (JSON), if present")
+    ap.add_argument("--make-traffic", metavar="DIR",
+                    help="write --traffic from rocprofv3 --pmc csv output under DIR/<COUNTER>_<kind>/ "
+                         "(COUNTER in FETCH_SIZE, WRITE_SIZE; kind in fwd, decode, copy) and exit")
     return ap.parse_args()
 
 
+# Kernels whose HBM bytes are reported, and the sources each one is built from: a traffic
+# figure taken from an older build of those sources is stale and reported as null.
+TRAFFIC_KERNELS = {
+    "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_internal.h"]),
+    "decode": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
+    "copy": (["copyBuffer"], []),
+}
+
+
+def sources_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_attention_31_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_means(folder, counter):
+    """Mean per-dispatch value of ``counter`` for each kernel name in a rocprofv3 csv run."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+                counts[name] = counts.get(name, 0) + 1
+    return {n: sums[n] / counts[n] for n in sums}
+
+
+def make_traffic(args):
+    """HBM bytes per launch = FETCH_SIZE·f_r + WRITE_SIZE·f_w (KiB), where f_r and f_w make the
+    counters of a plain 1 GiB copy read exactly 1 GiB and write exactly 1 GiB."""
+    def per_launch(kind, counter):
+        means = counter_means(os.path.join(args.make_traffic, f"{counter}_{kind}"), counter)
+        total = 0.0
+        for pat in TRAFFIC_KERNELS[kind][0]:
+            hits = [v for n, v in means.items() if pat in n]
+            if not hits:
+                raise SystemExit(f"no {counter} rows for {pat} under {args.make_traffic}")
+            total += max(hits)
+        return total
+
+    gib_kib = float(1 << 20)
+    f_r = gib_kib / per_launch("copy", "FETCH_SIZE")
+    f_w = gib_kib / per_launch("copy", "WRITE_SIZE")
+    out = {"method": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by a 1 GiB copy",
+           "fetch_scale": round(f_r, 4), "write_scale": round(f_w, 4)}
+    for kind in ("fwd", "decode"):
+        fk, wk = per_launch(kind, "FETCH_SIZE"), per_launch(kind, "WRITE_SIZE")
+        out[kind] = {"bytes_per_launch": round((fk * f_r + wk * f_w) * 1024.0),
+                     "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                     "kernels": TRAFFIC_KERNELS[kind][0],
+                     "sources_sha256": sources_digest(TRAFFIC_KERNELS[kind][1])}
+    with open(args.traffic, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def traffic_bytes(traffic, kind):
+    """Measured HBM bytes per launch, or None when absent or taken from other kernel sources."""
+    ent = traffic.get(kind)
+    if not isinstance(ent, dict) or ent.get("sources_sha256") != sources_digest(TRAFFIC_KERNELS[kind][1]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
 def cpu_baseline(wf, wd, q, k, v, qd, kd, vd, budget_s):
-    """Time the oracle (as it is) on a bounded sample: whole heads of each workload."""
+    """Time the oracle (as it is) on a bounded sample: whole heads of each workload, prefill
+    first (at most half the budget), then decode heads until the budget is spent."""
     threads = min(len(os.sched_getaffinity(0)), 16)
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ.setdefault(var, str(threads))
@@ -62,14 +139,14 @@ def cpu_baseline(wf, wd, q, k, v, qd, kd, vd, budget_s):
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     t0 = time.perf_counter()
     heads = 0
-    while heads < wf.H and time.perf_counter() - t0 < budget_s * 0.75:
+    while heads < wf.H and time.perf_counter() - t0 < budget_s * 0.5:
         attention_ref(qc[:, heads:heads + 1], kc[:, heads:heads + 1], vc[:, heads:heads + 1], wf.scale, wf.causal)
         heads += 1
     t_f = time.perf_counter() - t0
     flops = 4.0 * wf.N * wf.N * wf.d * heads / (2 if wf.causal else 1)
     t1 = time.perf_counter()
     dheads = 0
-    while dheads < wd.B * wd.H and time.perf_counter() - t1 < budget_s * 0.25:
+    while dheads < wd.B * wd.H and time.perf_counter() - t0 < budget_s:
         b, h = divmod(dheads, wd.H)
         decode_ref(qd[b:b + 1, h:h + 1].cpu(), kd[b:b + 1, h:h + 1].cpu(), vd[b:b + 1, h:h + 1].cpu(), wd.scale)
         dheads += 1
@@ -109,6 +186,8 @@ def copy_reference(torch, dev, args):
 
 def main():
     args = parse()
+    if args.make_traffic:
+        return make_traffic(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; the single-GPU figure is the measurement.", file=sys.stderr)
@@ -213,7 +292,7 @@ def main():
         out["roofline"] = {"kernel": "fa_fwd_kernel<128,true>", "bound": "mfma", "achieved": round(tf, 2),
                            "peak": round(MFMA_BF16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                           "traffic": traffic.get("fwd"), "algorithmic_bytes": fbytes}
+                           "traffic": traffic_bytes(traffic, "fwd"), "algorithmic_bytes": fbytes}
     if d_avg:
         gbs = dbytes / (d_avg * 1e-3) / 1e9
         out["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4), "ms_min": round(min(dec_ms), 4),
@@ -221,7 +300,7 @@ def main():
         out["roofline_decode"] = {"kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
                                   "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                  "traffic": traffic.get("decode"), "algorithmic_bytes": dbytes}
+                                  "traffic": traffic_bytes(traffic, "decode"), "algorithmic_bytes": dbytes}
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)

@@ -1,16 +1,19 @@
 // Fused exact-attention forward for CDNA4 (gfx950).
 //
-// One workgroup owns one (b, h, query block of 128 rows); blocks are
-// independent, so the grid runs over (b, h, query block) — the loop order
-// with the query block outside and the key/value tiles inside ([cicada]
-// §3.2.1–3.2.2; [15-779 L5] §5.1 and §6.3 "parallel over sequence length").
-// Per key tile j of 64 keys the workgroup:
-//   1. streams K_j, V_j from HBM into LDS (double-buffered: tile j+1 is in
-//      flight in registers while tile j is computed),
+// One workgroup of 8 wavefronts owns one (b, h, query block of 256 rows);
+// blocks are independent, so the grid runs over (b, h, query block) — the
+// loop order with the query block outside and the key/value tiles inside
+// ([cicada] §3.2.1–3.2.2; [15-779 L5] §5.1 and §6.3 "parallel over sequence
+// length").  Each wavefront owns 32 of the rows (split-Q, [15-779 L5] §6.4),
+// so every row's max and sums stay inside one wavefront.  Per key tile j of
+// 64 keys the workgroup:
+//   1. streams K_j, V_j from HBM into LDS: four buffers per tensor, filled by
+//      buffer loads that write LDS directly, each issued three iterations
+//      before the one that reads it,
 //   2. computes Sᵀ = K_j Q_iᵀ on bf16 MFMA with fp32 accumulation,
 //   3. masks keys after the query on tiles that cross the diagonal and keys
 //      past N on the ragged last tile ([15-779 L5] §6.2),
-//   4. keeps the running max m, the running sum ℓ and the output accumulator
+//   4. keeps the running max m, the running sums ℓ and the output accumulator
 //      consistent with each other — when m grows, ℓ and the accumulator are
 //      multiplied by exp(m_old − m_new) ([cicada] §3.2.2 steps B–D;
 //      [15-779 L5] §4.3–4.5),
@@ -21,28 +24,35 @@
 //
 // The reference max m is only moved when some row of the wavefront sees a
 // logit more than kRescaleLog2 (in log2 units) above it; otherwise the stale m
-// is kept for exponent and sum alike, which changes nothing in exact
+// is kept for exponent and sums alike, which changes nothing in exact
 // arithmetic (m cancels between ℓ and the accumulator) and bounds every P̃
 // by 2^kRescaleLog2.  This is the conditional rescaling of [cicada] §5
-// (FlashAttention-4), and it removes the accumulator multiply from almost
-// every tile.
+// (FlashAttention-4); it removes the accumulator multiply from almost every
+// tile.
 //
 // Pages cited: [cicada] "已有的几种大模型上下文支持情况"; [15-779 L5] "第 5 讲 ·
 // 案例：Transformer、注意力与 FlashAttention".
 //
-// Data layout on chip (per wavefront of 64 lanes, 32 query rows):
+// Layout on chip (one wavefront = 64 lanes, 32 query rows; two wavefronts per SIMD):
 // * The products are taken transposed — Sᵀ = K Qᵀ and Oᵀ = Vᵀ P̃ᵀ — so that
 //   with v_mfma_f32_32x32x16_bf16 each lane's accumulator column is one query
-//   row: the row max and row sum are in-lane plus one exchange between the two
-//   32-lane halves (v_permlane32_swap), the rescale factor is a per-lane
+//   row: the row max and row sums are in-lane plus one exchange between the
+//   two 32-lane halves (v_permlane32_swap), the rescale factor is a per-lane
 //   scalar, and the fp32 scores of Sᵀ are already laid out as the B operand of
 //   the second product (converted to bf16 in place, no LDS round trip).
-// * K tile in LDS: row-major [key][d], rows padded to 2d+16 bytes so the MFMA
-//   operand reads (16 rows × 16 bytes per pass) hit distinct banks.
-// * V tile in LDS: row-major [key][d], rows padded to 2d+64 bytes; the Vᵀ
+// * K tile in LDS: row-major [key][d] in 16-byte chunks, the chunk index
+//   XOR-ed with a function of the row so that the operand reads (16 rows ×
+//   one chunk per pass) hit distinct banks; the direct loads write whole
+//   1 KiB runs, each lane fetching the global chunk that belongs in its slot.
+// * V tile in LDS: row-major [key][d], chunk index XOR-ed likewise; the Vᵀ
 //   operand, whose reduction index is the key, is read with the LDS transpose
 //   load ds_read_b64_tr_b16, four keys per 16-lane group.
-// * All per-lane LDS addresses are a lane base plus compile-time offsets.
+// * The eight tile buffers are separate LDS objects, so the compiler can tell
+//   that a direct load into one buffer never aliases reads of another and
+//   lets those reads run while the loads are in flight.
+// * Software pipeline: while the vector unit turns the scores of tile j into
+//   probabilities, the matrix unit already computes the scores of tile j+1;
+//   the row max of tile j+1 is taken while Oᵀ += Vᵀ_j P̃ᵀ_j runs.
 // * exp is computed as exp2 with scale·log2(e) folded into the logits.
 
 #include <hip/hip_runtime.h>
@@ -66,6 +76,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // log2-domain growth of the running max that forces a rescale.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr int kStages = 4;  // LDS buffers per tensor (the loop is unrolled by this)
 
 template <int D>
 struct Tile {
@@ -74,6 +85,7 @@ struct Tile {
   static constexpr int ROW = 2 * D;               // bytes per K/V row in LDS (unpadded)
   static constexpr int TILE_BYTES = BN * ROW;     // one K or V tile
   static constexpr int LOADS = TILE_BYTES / (16 * kFwdThreads);  // 16-byte direct loads per thread per tile
+  static constexpr int LDS_BYTES = 2 * kStages * TILE_BYTES;
   static constexpr int NSUB = BN / 32;            // 32-key sub-tiles of Sᵀ
   static constexpr int KS_QK = D / 16;            // MFMA k-steps of Sᵀ = K Qᵀ
   static constexpr int DSUB = D / 32;             // 32-row sub-tiles of Oᵀ
@@ -120,6 +132,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
+// s_waitcnt that waits until at most n vector-memory loads are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+template <int n>
+__device__ inline void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Work index -> (bh, query block).  Workgroups are dealt round-robin to the
 // 8 XCDs; with xcd_remap each XCD receives whole heads (so a head's K/V stays
 // in one L2), and inside an XCD's share the heaviest query blocks (the last
@@ -142,15 +162,14 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
-  // Four separate LDS objects: with distinct objects the compiler can tell
-  // that the direct loads filling one buffer never alias reads of another,
-  // and does not hold those reads back until the loads complete.
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES];
-  unsigned char* const kbuf[2] = {k_lds0, k_lds1};
-  unsigned char* const vbuf[2] = {v_lds0, v_lds1};
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES],
+      k_lds2[T::TILE_BYTES], k_lds3[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES],
+      v_lds2[T::TILE_BYTES], v_lds3[T::TILE_BYTES];
+  unsigned char* const kbufs[4] = {k_lds0, k_lds1, k_lds2, k_lds3};
+  unsigned char* const vbufs[4] = {v_lds0, v_lds1, v_lds2, v_lds3};
 
   int bh, qb;
   decode_work(p, bh, qb);
@@ -315,46 +334,56 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
       }
   };
 
-  // ---- pipeline: K runs two tiles ahead of the softmax, V one tile ahead -------------
-  // Iteration j reads K_{j+1} (kbuf[(j+1)&1]) and V_j (vbuf[j&1]) and fills
-  // K_{j+2} -> kbuf[j&1], V_{j+1} -> vbuf[(j+1)&1]: every buffer written in
-  // iteration j was last read before the barrier that ended iteration j-1.
-  // Within an iteration the MFMAs of Sᵀ_{j+1} are issued between the exp2 /
-  // convert / sum instructions of tile j, so the matrix and vector units run
-  // side by side; the row max of Sᵀ_{j+1} is taken while Oᵀ += Vᵀ_j P̃ᵀ_j runs.
+  // ---- pipeline ---------------------------------------------------------------------
+  // Iteration j reads K_{j+1} (for Sᵀ_{j+1}) and V_j, and issues the loads of
+  // K_{j+4} into the buffer K_j held and of V_{j+3} into the buffer V_{j-1}
+  // held: both were last read before the barrier that ended iteration j-1.
+  // Before its closing barrier, iteration j waits only for the loads issued
+  // two iterations earlier (K_{j+2}, V_{j+1}: needed next), so every load has
+  // about two iterations to arrive.  Within an iteration the MFMAs of Sᵀ_{j+1}
+  // are issued between the exp2 / convert / sum instructions of tile j, so the
+  // matrix and vector units run side by side; the row max of Sᵀ_{j+1} is taken
+  // while Oᵀ += Vᵀ_j P̃ᵀ_j runs.  The loop is unrolled by kStages so that every
+  // buffer address is a compile-time offset.
   f32x16_t s0[T::NSUB], s1[T::NSUB];
-  load_tile(krsrc, k_goff, 0, kbuf[0]);
-  load_tile(vrsrc, v_goff, 0, vbuf[0]);
-  if (n_tiles > 1) load_tile(krsrc, k_goff, T::BN, kbuf[1]);
-  __builtin_amdgcn_s_waitcnt(0);
+  auto kb = [&](int j) { return kbufs[j % kStages]; };
+  auto vb = [&](int j) { return vbufs[j % kStages]; };
+#pragma unroll
+  for (int j = 0; j < kStages; ++j)
+    if (j < n_tiles) load_tile(krsrc, k_goff, j * T::BN, kb(j));
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < n_tiles) load_tile(vrsrc, v_goff, j * T::BN, vb(j));
+  wait_vmcnt<0>();
   __syncthreads();
   if (active(0)) {
-    qk(kbuf[0], s0);
+    qk(kb(0), s0);
     mask(0, s0);
     rescale(rowmax(s0));
   }
-  __syncthreads();  // every wave is done with kbuf[0] before K_2 lands in it
+  __syncthreads();  // every wave is done with K_0 before K_4 lands in its buffer
 
   // Tiles 0 .. n_clean-1 need no mask for any row of the workgroup (and, when
   // causal, are seen by every wavefront); iterations whose next tile is clean
   // run without mask or activity tests.
   const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
 
-  // kmine/vmine: the buffers this iteration fills (K_{j+2}, V_{j+1});
-  // kread/vread: the ones it reads (K_{j+1}, V_j).  Called with the two
-  // orders alternately, so every buffer address is a constant after inlining.
-  auto iteration = [&](int j, unsigned char* kmine, const unsigned char* kread, unsigned char* vmine,
-                       const unsigned char* vread, f32x16_t(&scur)[T::NSUB], f32x16_t(&snext)[T::NSUB],
-                       auto generic) {
+  // phase: j mod kStages as a compile-time constant
+  auto iteration = [&](int j, auto phase, auto generic) {
+    constexpr int P = decltype(phase)::value;
     constexpr bool GENERIC = decltype(generic)::value;
-    if (j + 2 < n_tiles) load_tile(krsrc, k_goff, (j + 2) * T::BN, kmine);
-    if (j + 1 < n_tiles) load_tile(vrsrc, v_goff, (j + 1) * T::BN, vmine);
+    f32x16_t(&scur)[T::NSUB] = (P & 1) ? s1 : s0;
+    f32x16_t(&snext)[T::NSUB] = (P & 1) ? s0 : s1;
+    const bool ld_k = j + kStages < n_tiles;
+    const bool ld_v = j + kStages - 1 < n_tiles;
+    if (ld_k) load_tile(krsrc, k_goff, (j + kStages) * T::BN, kb(P));
+    if (ld_v) load_tile(vrsrc, v_goff, (j + kStages - 1) * T::BN, vb(P + kStages - 1));
     const bool next = GENERIC ? (j + 1 < n_tiles && active(j + 1)) : true;
     const bool cur = GENERIC ? active(j) : true;
     if (cur) {
       u32x4_t pw[T::KS_PV];
       if (next) {
-        qk(kread, snext);
+        qk(kb(P + 1), snext);
         exps(scur, pw);
         // issue order: K-fragment reads run two MFMAs ahead; each MFMA of
         // Sᵀ_{j+1} is followed by six VALU instructions of tile j's softmax
@@ -368,24 +397,45 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
       } else {
         exps(scur, pw);
       }
-      pv(vread, pw);
+      pv(vb(P), pw);
     }
     // (a wavefront that sees no key of tile j sees none of tile j+1 either)
     if (cur && next) {
       if (GENERIC) mask(j + 1, snext);
       rescale(rowmax(snext));
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // loads issued by this iteration and the one before may stay in flight
+    const int pending = (ld_k ? 1 : 0) + (ld_v ? 1 : 0) + (j + kStages - 1 < n_tiles ? 1 : 0) +
+                        (j + kStages - 2 < n_tiles && j >= 1 ? 1 : 0);
+    if (pending >= 4)
+      wait_vmcnt<4 * T::LOADS>();
+    else if (pending == 3)
+      wait_vmcnt<3 * T::LOADS>();
+    else if (pending == 2)
+      wait_vmcnt<2 * T::LOADS>();
+    else if (pending == 1)
+      wait_vmcnt<T::LOADS>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
   };
   int j = 0;
-  for (; j + 2 < n_clean; j += 2) {
-    iteration(j, kbuf[0], kbuf[1], vbuf[1], vbuf[0], s0, s1, std::false_type{});
-    iteration(j + 1, kbuf[1], kbuf[0], vbuf[0], vbuf[1], s1, s0, std::false_type{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  static_assert(kStages == 4, "unrolled by four");
+  for (; j + 4 < n_clean; j += 4) {
+    iteration(j, I0{}, std::false_type{});
+    iteration(j + 1, I1{}, std::false_type{});
+    iteration(j + 2, I2{}, std::false_type{});
+    iteration(j + 3, I3{}, std::false_type{});
   }
-  for (; j < n_tiles; j += 2) {
-    iteration(j, kbuf[0], kbuf[1], vbuf[1], vbuf[0], s0, s1, std::true_type{});
-    if (j + 1 < n_tiles) iteration(j + 1, kbuf[1], kbuf[0], vbuf[0], vbuf[1], s1, s0, std::true_type{});
+  for (; j < n_tiles; j += 4) {
+    iteration(j, I0{}, std::true_type{});
+    if (j + 1 < n_tiles) iteration(j + 1, I1{}, std::true_type{});
+    if (j + 2 < n_tiles) iteration(j + 2, I2{}, std::true_type{});
+    if (j + 3 < n_tiles) iteration(j + 3, I3{}, std::true_type{});
   }
 
   // ---- epilogue: one division, one store of O and L ------------------------------
@@ -411,6 +461,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   using T = Tile<D>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - T::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const dim3 grid(p.BH * p.n_qblk);
   hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();

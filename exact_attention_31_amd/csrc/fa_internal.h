@@ -8,10 +8,10 @@
 
 namespace fa {
 
-// Prefill tiling: a workgroup of 4 wavefronts owns 128 query rows (32 per
+// Prefill tiling: a workgroup of 8 wavefronts owns 256 query rows (32 per
 // wavefront, split-Q: every row's reductions stay inside one wavefront); key
 // tiles hold 64 keys.
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBlockM = 32 * kFwdWaves;
 

@@ -92,9 +92,11 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Lkv, int d, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of (query block, key tile) pairs fa_fwd processes for one (b, h):
- * with T tiles per side this is T(T+1)/2 when causal and T² otherwise, the
- * tiles wholly above the diagonal being skipped ([15-779 L5] §6.2).
+/* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
+ * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not
+ * causal; when causal, query block i visits only the key tiles up to its last
+ * row, the tiles wholly above the diagonal being skipped ([15-779 L5] §6.2)
+ * (T(T+1)/2 of T² for square tiles).
  * Host-only; returns -1 for invalid arguments. */
 long long fa_fwd_tile_pairs(int N, int d, int causal);
 

@@ -95,8 +95,8 @@ def test_decode_argument_checks():
 
 def test_tile_shape():
     _lib()
-    assert fa.fa_fwd_tile_shape(128) == (128, 64)
-    assert fa.fa_fwd_tile_shape(64) == (128, 64)
+    assert fa.fa_fwd_tile_shape(128) == (256, 64)
+    assert fa.fa_fwd_tile_shape(64) == (256, 64)
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile_shape(80)
 
