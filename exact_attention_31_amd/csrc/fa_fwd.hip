@@ -8,8 +8,7 @@
 // so every row's max and sums stay inside one wavefront.  Per key tile j of
 // 64 keys the workgroup:
 //   1. streams K_j, V_j from HBM into LDS: four buffers per tensor, filled by
-//      buffer loads that write LDS directly, each issued three iterations
-//      before the one that reads it,
+//      buffer loads that write LDS directly, about three tiles ahead of use,
 //   2. computes Sᵀ = K_j Q_iᵀ on bf16 MFMA with fp32 accumulation,
 //   3. masks keys after the query on tiles that cross the diagonal and keys
 //      past N on the ragged last tile ([15-779 L5] §6.2),
@@ -33,7 +32,15 @@
 // Pages cited: [cicada] "已有的几种大模型上下文支持情况"; [15-779 L5] "第 5 讲 ·
 // 案例：Transformer、注意力与 FlashAttention".
 //
-// Layout on chip (one wavefront = 64 lanes, 32 query rows; two wavefronts per SIMD):
+// Schedule: the work of a tile is split into a softmax phase Y (steps 3–4 and
+// P̃: vector ALU only) and a matrix phase X (step 5 for tile j and step 2 for
+// tile j+1: MFMAs and LDS reads only).  Each wavefront runs Y(0) X(0) Y(1)
+// X(1) ..., one phase per workgroup barrier; wavefronts 4-7 start one barrier
+// after wavefronts 0-3.  The two wavefronts that share a SIMD are therefore
+// always in opposite phases: while one keeps the matrix core busy, the other
+// runs exp2 and the sums on the vector ALU.
+//
+// Layout on chip (one wavefront = 64 lanes, 32 query rows):
 // * The products are taken transposed — Sᵀ = K Qᵀ and Oᵀ = Vᵀ P̃ᵀ — so that
 //   with v_mfma_f32_32x32x16_bf16 each lane's accumulator column is one query
 //   row: the row max and row sums are in-lane plus one exchange between the
@@ -50,9 +57,6 @@
 // * The eight tile buffers are separate LDS objects, so the compiler can tell
 //   that a direct load into one buffer never aliases reads of another and
 //   lets those reads run while the loads are in flight.
-// * Software pipeline: while the vector unit turns the scores of tile j into
-//   probabilities, the matrix unit already computes the scores of tile j+1;
-//   the row max of tile j+1 is taken while Oᵀ += Vᵀ_j P̃ᵀ_j runs.
 // * exp is computed as exp2 with scale·log2(e) folded into the logits.
 
 #include <hip/hip_runtime.h>
@@ -77,6 +81,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // log2-domain growth of the running max that forces a rescale.
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kStages = 4;  // LDS buffers per tensor (the loop is unrolled by this)
+constexpr int kOperandLead = 2;  // MFMA pairs by which LDS operand reads run ahead
 
 template <int D>
 struct Tile {
@@ -140,6 +145,18 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier without a memory fence: __syncthreads() orders all memory
+// and therefore waits for every outstanding load, including the direct-to-LDS
+// loads of tiles that are not needed yet.  LDS written by those loads is read
+// only after the writer's own s_waitcnt and this barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ inline void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Work index -> (bh, query block).  Workgroups are dealt round-robin to the
 // 8 XCDs; with xcd_remap each XCD receives whole heads (so a head's K/V stays
 // in one L2), and inside an XCD's share the heaviest query blocks (the last
@@ -180,23 +197,24 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   const int i32 = lane & 31;  // query column of Sᵀ / Oᵀ owned by this lane
   const int g = lane >> 5;    // which 32-lane half
   const int jj = lane & 15;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
   const int q0 = qb * kFwdBlockM;
-  const int wq0 = q0 + wave * 32;  // first query row of this wavefront
+  const int wq0 = q0 + wave_u * 32;  // first query row of this wavefront (uniform)
   const int q_row = wq0 + i32;
   const size_t base = (size_t)bh * N * D;
+  const int grp = wave_u >> 2;  // wavefronts w and w+4 share a SIMD and alternate phases
 
   // Direct global->LDS loads: wavefront `wave`, load i fills LDS chunk slots
-  // (i*4 + wave)*64 + lane of the tile; the slot's (row, swizzled chunk) names
+  // (i*8 + wave)*64 + lane of the tile; the slot's (row, swizzled chunk) names
   // the global chunk this lane fetches.  Load i covers rows r0 + i*RPL, and
   // both swizzles repeat with that period, so load i is load 0 shifted by
-  // i*RPL rows.
+  // i*RPL rows.  Rows past N lie past the head's bytes and read as zero (their
+  // logits are masked).
   constexpr int RPL = kFwdWaves * 64 / T::CH;  // rows covered by one load across the workgroup
   const int r0 = (wave * 64 + lane) / T::CH;
   const int cpos = lane % T::CH;
   const int k_goff = r0 * T::ROW + ((cpos ^ T::k_swz(r0)) << 4);
   const int v_goff = r0 * T::ROW + ((cpos ^ T::v_swz(r0)) << 4);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
-  // rows past N lie past the head's bytes and read as zero (their logits are masked)
   const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int goff, int kv0, unsigned char* dst) {
@@ -206,7 +224,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   };
 
   // Operand-read lane offsets (bytes within a tile).
-  int k_rd[T::KS_QK];  // Kᵀ rows i32 (+32 per sub-tile), chunk 2kk + g
+  int k_rd[T::KS_QK];  // K rows i32 (+32 per sub-tile), chunk 2kk + g
 #pragma unroll
   for (int kk = 0; kk < T::KS_QK; ++kk) k_rd[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::k_swz(i32)) << 4);
   int v_rd[T::DSUB];   // transpose reads: rows 4g + jj/4 (+16kk, +8), dims 32ds + 16(G&1) + 4(jj&3)
@@ -242,25 +260,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   f32x16_t acc[T::DSUB];
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
+  f32x16_t s[T::NSUB];       // scores of the tile between its QK and its softmax
+  u32x4_t pw[T::KS_PV];      // P̃ of the tile between its softmax and its PV
 
-  // ---- Sᵀ = K Qᵀ for one tile (the two 32-key sub-tiles interleaved) ----------------
-  auto qk = [&](const unsigned char* kb, f32x16_t (&s)[T::NSUB]) {
-#pragma unroll
-    for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < T::KS_QK; ++kk)
-#pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + k_rd[kk] + sub * 32 * T::ROW);
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], s[sub], 0, 0, 0);
-      }
-  };
-
-  // ---- mask of one tile's scores: keys after the query (diagonal tiles), keys
-  //      past N (last tile); only tiles at the end of the key range need it
-  auto mask = [&](int j, f32x16_t (&s)[T::NSUB]) {
+  // ---- softmax phase of tile j: mask, row max, rescale, P̃ and the sums ------------
+  auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
     const int kv0 = j * T::BN;
-    if ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0)) {
+    if (!decltype(clean)::value && ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0))) {
       const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub)
@@ -270,19 +276,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
           if (key > lim) s[sub][r] = -INFINITY;
         }
     }
-  };
-  // ---- row max of one tile's scores ------------------------------------------------------
-  auto rowmax = [&](const f32x16_t (&s)[T::NSUB]) {
-    float mt = -INFINITY;
+    // row max: four independent chains, then across the two lane halves
+    float mx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
-    return pair_max(mt);
-  };
-  // ---- move the reference max when some row outgrew it by 2^kRescaleLog2 ----------------
-  auto rescale = [&](float mt) {
-    // The first tile holds key 0, visible to every row: m is finite after it.
+      for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[sub][r]);
+    const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+    // move the reference max only when some row outgrew it by 2^kRescaleLog2;
+    // the first tile holds key 0, visible to every row, so m is finite after it
     if (__any((mt - m) * c > kRescaleLog2)) {
       const float m_new = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
@@ -292,13 +296,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
       m = m_new;
     }
-  };
-
-  // ---- P̃ = exp2(s·c − m·c) as packed bf16, and the two row sums -------------------------
-  auto exps = [&](const f32x16_t (&s)[T::NSUB], u32x4_t (&pw)[T::KS_PV]) {
     const float mc = m * c;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs = 0.f, rsb = 0.f;
+    float rs[2] = {0.f, 0.f}, rsb[2] = {0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < T::KS_PV; ++kk) {
       const int h8 = (kk & 1) * 8;
@@ -306,107 +306,93 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
         const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
-        rs += e0 + e1;
+        rs[e & 1] += e0 + e1;
         // The pair goes to dot2 directly: fed from an element of the packed
         // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
         bf16x2_t pe;
         pe[0] = (__bf16)e0;
         pe[1] = (__bf16)e1;
-        rsb = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb, false);
+        rsb[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb[e & 1], false);
         pw[kk][e] = __builtin_bit_cast(uint32_t, pe);
       }
     }
-    l += rs;
-    lb += rsb;
+    l += rs[0] + rs[1];
+    lb += rsb[0] + rsb[1];
   };
 
-  // ---- Oᵀ += Vᵀ P̃ᵀ ----------------------------------------------------------------------
-  auto pv = [&](const unsigned char* vb, const u32x4_t (&pw)[T::KS_PV]) {
+  // ---- matrix phase: Oᵀ += Vᵀ_j P̃ᵀ_j and Sᵀ_{j+1} = K_{j+1} Qᵀ, MFMAs interleaved ------
+  auto qk_step = [&](const unsigned char* kb, int i) __attribute__((always_inline)) {
+    const int kk = i / T::NSUB, sub = i % T::NSUB;
+    const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + k_rd[kk] + sub * 32 * T::ROW);
+    s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], s[sub], 0, 0, 0);
+  };
+  auto pv_step = [&](const unsigned char* vb, int i) __attribute__((always_inline)) {
+    const int kk = i / T::DSUB, ds = i % T::DSUB;
+    const u32x2_t a0 = lds_tr_read(vb, v_rd[ds] + 16 * kk * T::ROW);
+    const u32x2_t a1 = lds_tr_read(vb, v_rd[ds] + (16 * kk + 8) * T::ROW);
+    const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, pw[kk]), acc[ds], 0, 0, 0);
+  };
+  constexpr int NQK = T::KS_QK * T::NSUB;  // MFMAs of one Sᵀ tile
+  constexpr int NPV = T::KS_PV * T::DSUB;  // MFMAs of one Oᵀ update
+  auto matrix_clean = [&](const unsigned char* vb, const unsigned char* kb) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);  // the matrix-phase wavefront wins issue ties
+    // Lane offsets opaque to loop-invariant code motion: addresses are formed
+    // here as offset + constant, the constant going into the instruction.
 #pragma unroll
-    for (int kk = 0; kk < T::KS_PV; ++kk)
+    for (int kk = 0; kk < T::KS_QK; ++kk) asm volatile("" : "+v"(k_rd[kk]));
 #pragma unroll
-      for (int ds = 0; ds < T::DSUB; ++ds) {
-        const u32x2_t a0 = lds_tr_read(vb, v_rd[ds] + 16 * kk * T::ROW);
-        const u32x2_t a1 = lds_tr_read(vb, v_rd[ds] + (16 * kk + 8) * T::ROW);
-        const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-        acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          __builtin_bit_cast(bf16x8_t, pw[kk]), acc[ds], 0, 0, 0);
-      }
+    for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(v_rd[ds]));
+#pragma unroll
+    for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
+    static_assert(NQK == NPV, "interleave pairs one MFMA of each product");
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      qk_step(kb, i);
+      pv_step(vb, i);
+    }
+    // issue order: the operand reads run kOperandLead MFMA pairs ahead of
+    // their MFMAs (one K read and two Vᵀ transpose reads per pair)
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kOperandLead, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto matrix = [&](const unsigned char* vb, const unsigned char* kb, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+    if (do_qk) {
+#pragma unroll
+      for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) qk_step(kb, i);
+    }
+    if (do_pv) {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) pv_step(vb, i);
+    }
   };
 
-  // ---- pipeline ---------------------------------------------------------------------
-  // Iteration j reads K_{j+1} (for Sᵀ_{j+1}) and V_j, and issues the loads of
-  // K_{j+4} into the buffer K_j held and of V_{j+3} into the buffer V_{j-1}
-  // held: both were last read before the barrier that ended iteration j-1.
-  // Before its closing barrier, iteration j waits only for the loads issued
-  // two iterations earlier (K_{j+2}, V_{j+1}: needed next), so every load has
-  // about two iterations to arrive.  Within an iteration the MFMAs of Sᵀ_{j+1}
-  // are issued between the exp2 / convert / sum instructions of tile j, so the
-  // matrix and vector units run side by side; the row max of Sᵀ_{j+1} is taken
-  // while Oᵀ += Vᵀ_j P̃ᵀ_j runs.  The loop is unrolled by kStages so that every
-  // buffer address is a compile-time offset.
-  f32x16_t s0[T::NSUB], s1[T::NSUB];
-  auto kb = [&](int j) { return kbufs[j % kStages]; };
-  auto vb = [&](int j) { return vbufs[j % kStages]; };
-#pragma unroll
-  for (int j = 0; j < kStages; ++j)
-    if (j < n_tiles) load_tile(krsrc, k_goff, j * T::BN, kb(j));
-#pragma unroll
-  for (int j = 0; j < kStages - 1; ++j)
-    if (j < n_tiles) load_tile(vrsrc, v_goff, j * T::BN, vb(j));
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (active(0)) {
-    qk(kb(0), s0);
-    mask(0, s0);
-    rescale(rowmax(s0));
-  }
-  __syncthreads();  // every wave is done with K_0 before K_4 lands in its buffer
-
-  // Tiles 0 .. n_clean-1 need no mask for any row of the workgroup (and, when
-  // causal, are seen by every wavefront); iterations whose next tile is clean
-  // run without mask or activity tests.
-  const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
-
-  // phase: j mod kStages as a compile-time constant
-  auto iteration = [&](int j, auto phase, auto generic) {
-    constexpr int P = decltype(phase)::value;
-    constexpr bool GENERIC = decltype(generic)::value;
-    f32x16_t(&scur)[T::NSUB] = (P & 1) ? s1 : s0;
-    f32x16_t(&snext)[T::NSUB] = (P & 1) ? s0 : s1;
-    const bool ld_k = j + kStages < n_tiles;
-    const bool ld_v = j + kStages - 1 < n_tiles;
-    if (ld_k) load_tile(krsrc, k_goff, (j + kStages) * T::BN, kb(P));
-    if (ld_v) load_tile(vrsrc, v_goff, (j + kStages - 1) * T::BN, vb(P + kStages - 1));
-    const bool next = GENERIC ? (j + 1 < n_tiles && active(j + 1)) : true;
-    const bool cur = GENERIC ? active(j) : true;
-    if (cur) {
-      u32x4_t pw[T::KS_PV];
-      if (next) {
-        qk(kb(P + 1), snext);
-        exps(scur, pw);
-        // issue order: K-fragment reads run two MFMAs ahead; each MFMA of
-        // Sᵀ_{j+1} is followed by six VALU instructions of tile j's softmax
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < T::KS_QK * T::NSUB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      } else {
-        exps(scur, pw);
-      }
-      pv(vb(P), pw);
-    }
-    // (a wavefront that sees no key of tile j sees none of tile j+1 either)
-    if (cur && next) {
-      if (GENERIC) mask(j + 1, snext);
-      rescale(rowmax(snext));
-    }
-    // loads issued by this iteration and the one before may stay in flight
-    const int pending = (ld_k ? 1 : 0) + (ld_v ? 1 : 0) + (j + kStages - 1 < n_tiles ? 1 : 0) +
-                        (j + kStages - 2 < n_tiles && j >= 1 ? 1 : 0);
+  // ---- pipeline -------------------------------------------------------------------
+  // Every wavefront runs the same sequence of phases, each closed by a
+  // workgroup barrier:  QK(0) | Y(0) | X(0) | Y(1) | X(1) | ... | Y(n-1) | X(n-1)
+  // with Y(j) the softmax of tile j and X(j) the matrix phase Oᵀ += Vᵀ_j P̃ᵀ_j,
+  // Sᵀ_{j+1} = K_{j+1} Qᵀ.  Group 1 (wavefronts 4-7) starts one barrier later
+  // than group 0, so the two wavefronts of a SIMD are always in opposite
+  // phases: one feeds the matrix core while the other runs the softmax.
+  // Loads go by the global phase T (group 0's phase index; group 1's plus one).
+  // Batch b (K_{b+4}, V_{b+3}) is issued at T = 2b+2, into the buffers that
+  // K_b and V_{b-1} left at T = 2b+1, and must be complete when T = 2b+8
+  // begins (group 0's X(b+3)): group 0 waits for it at the end of Y(b+3),
+  // group 1 at the end of X(b+2).
+  auto kb = [&](int j) { return kbufs[j & 3]; };
+  auto vb = [&](int j) { return vbufs[j & 3]; };
+  auto batch_tiles = [&](int b) { return (b + 4 < n_tiles ? 1 : 0) + (b + 3 >= 0 && b + 3 < n_tiles ? 1 : 0); };
+  auto wait_batches = [&](int pending) {  // at most `pending` tiles of loads outstanding
     if (pending >= 4)
       wait_vmcnt<4 * T::LOADS>();
     else if (pending == 3)
@@ -417,26 +403,72 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       wait_vmcnt<T::LOADS>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
   };
-  int j = 0;
+  auto issue_batch = [&](int b, auto phase) __attribute__((always_inline)) {
+    constexpr int P = decltype(phase)::value;  // b mod 4
+    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(P));
+    if (b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(P + 3));
+  };
+#pragma unroll
+  for (int b = -4; b < 0; ++b) {
+    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(b + 4));
+    if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(b + 3));
+  }
+  wait_batches(batch_tiles(-3) + batch_tiles(-2) + batch_tiles(-1));
+  // The Q loads were issued before the tile loads, so they are complete now;
+  // a use here settles the compiler's load tracking for those registers once,
+  // instead of a full wait for all loads at their first use inside the loop.
+#pragma unroll
+  for (int kk = 0; kk < T::KS_QK; ++kk) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[kk])));
+  block_barrier();
+  if (grp == 1) block_barrier();
+  if (active(0)) matrix(vb(0), kb(0), false, true);
+  if (grp == 1) wait_batches(batch_tiles(-2) + batch_tiles(-1));
+  block_barrier();
+
+  auto iter = [&](int j, auto phase, auto clean) __attribute__((always_inline)) {
+    constexpr int P = decltype(phase)::value;  // j mod 4
+    constexpr bool CLEAN = decltype(clean)::value;
+    // Y(j)
+    if (grp == 1) issue_batch(j, phase);
+    if (CLEAN)
+      softmax(j, std::true_type{});
+    else if (active(j))
+      softmax(j, std::false_type{});
+    if (grp == 0) wait_batches(batch_tiles(j - 2) + batch_tiles(j - 1));
+    block_barrier();
+    // X(j)
+    if (CLEAN)
+      matrix_clean(vb(P), kb(P + 1));
+    else
+      matrix(vb(P), kb(P + 1), active(j), j + 1 < n_tiles && active(j + 1));
+    if (grp == 0) issue_batch(j, phase);
+    if (grp == 1) wait_batches(batch_tiles(j - 1) + batch_tiles(j));
+    block_barrier();
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  static_assert(kStages == 4, "unrolled by four");
-  for (; j + 4 < n_clean; j += 4) {
-    iteration(j, I0{}, std::false_type{});
-    iteration(j + 1, I1{}, std::false_type{});
-    iteration(j + 2, I2{}, std::false_type{});
-    iteration(j + 3, I3{}, std::false_type{});
+  using Y = std::true_type;
+  using G = std::false_type;
+  // Tiles 0 .. n_clean-1 are seen whole by every row of the workgroup;
+  // iteration j is clean when tiles j and j+1 are.
+  const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  int j = 0;
+  for (; j + 4 <= n_clean - 1; j += 4) {
+    iter(j, I0{}, Y{});
+    iter(j + 1, I1{}, Y{});
+    iter(j + 2, I2{}, Y{});
+    iter(j + 3, I3{}, Y{});
   }
   for (; j < n_tiles; j += 4) {
-    iteration(j, I0{}, std::true_type{});
-    if (j + 1 < n_tiles) iteration(j + 1, I1{}, std::true_type{});
-    if (j + 2 < n_tiles) iteration(j + 2, I2{}, std::true_type{});
-    if (j + 3 < n_tiles) iteration(j + 3, I3{}, std::true_type{});
+    iter(j, I0{}, G{});
+    if (j + 1 < n_tiles) iter(j + 1, I1{}, G{});
+    if (j + 2 < n_tiles) iter(j + 2, I2{}, G{});
+    if (j + 3 < n_tiles) iter(j + 3, I3{}, G{});
   }
+  if (grp == 0) block_barrier();
 
   // ---- epilogue: one division, one store of O and L ------------------------------
   l = pair_sum(l);
