@@ -26,8 +26,12 @@
 // is kept for exponent and sums alike, which changes nothing in exact
 // arithmetic (m cancels between ℓ and the accumulator) and bounds every P̃
 // by 2^kRescaleLog2.  This is the conditional rescaling of [cicada] §5
-// (FlashAttention-4); it removes the accumulator multiply from almost every
-// tile.
+// (FlashAttention-4), with the threshold set by the range of fp32 and bf16
+// rather than by their precision (which is relative, so a stale m costs no
+// accuracy).  P̃ is computed against the current m first; a tile row sum
+// within 2^kRescaleLog2 proves that no element exceeds it, and only otherwise
+// (in practice the first tile, where m = −∞) is the row max taken, m moved
+// and P̃ recomputed.
 //
 // Pages cited: [cicada] "已有的几种大模型上下文支持情况"; [15-779 L5] "第 5 讲 ·
 // 案例：Transformer、注意力与 FlashAttention".
@@ -78,8 +82,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// log2-domain growth of the running max that forces a rescale.
-constexpr float kRescaleLog2 = 8.0f;
+// log2-domain growth of the running max that forces a rescale.  P̃ stays
+// below 2^48, so the fp32 accumulator holds Σ P̃·v over the at most 2^24 keys
+// the library accepts as long as |v| < 2^56.
+constexpr float kRescaleLog2 = 48.0f;
+// A tile's P̃ row sum at most this bounds each of its elements by 2^kRescaleLog2.
+constexpr float kSumBound = 281474976710656.0f;  // 2^48
 constexpr int kStages = 4;  // LDS buffers per tensor (the loop is unrolled by this)
 constexpr int kOperandLead = 2;  // MFMA pairs by which LDS operand reads run ahead
 
@@ -210,17 +218,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   // both swizzles repeat with that period, so load i is load 0 shifted by
   // i*RPL rows.  Rows past N lie past the head's bytes and read as zero (their
   // logits are masked).
-  constexpr int RPL = kFwdWaves * 64 / T::CH;  // rows covered by one load across the workgroup
-  const int r0 = (wave * 64 + lane) / T::CH;
+  constexpr int RPL = (kFwdWaves / 2) * 64 / T::CH;  // rows covered by one load across group 1
+  const int r0 = ((wave & 3) * 64 + lane) / T::CH;
   const int cpos = lane % T::CH;
   const int k_goff = r0 * T::ROW + ((cpos ^ T::k_swz(r0)) << 4);
   const int v_goff = r0 * T::ROW + ((cpos ^ T::v_swz(r0)) << 4);
   const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int goff, int kv0, unsigned char* dst) {
-    unsigned char* d = dst + wave_u * 1024;
+    unsigned char* d = dst + (wave_u & 3) * 1024;
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) load_lds16(rsrc, d + i * kFwdWaves * 1024, goff, (kv0 + i * RPL) * T::ROW);
+    for (int i = 0; i < 2 * T::LOADS; ++i) load_lds16(rsrc, d + i * (kFwdWaves / 2) * 1024, goff, (kv0 + i * RPL) * T::ROW);
   };
 
   // Operand-read lane offsets (bytes within a tile).
@@ -276,48 +284,60 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
           if (key > lim) s[sub][r] = -INFINITY;
         }
     }
-    // row max: four independent chains, then across the two lane halves
-    float mx[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < T::NSUB; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[sub][r]);
-    const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-    // move the reference max only when some row outgrew it by 2^kRescaleLog2;
-    // the first tile holds key 0, visible to every row, so m is finite after it
-    if (__any((mt - m) * c > kRescaleLog2)) {
-      const float m_new = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-      l *= alpha;
-      lb *= alpha;
-#pragma unroll
-      for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
-      m = m_new;
-    }
-    const float mc = m * c;
+    // P̃ against the current reference max; the tile sum bounds every element,
+    // so a sum at most 2^kRescaleLog2 proves that no row outgrew m by more
+    // than that and the row max is not needed.
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs[2] = {0.f, 0.f}, rsb[2] = {0.f, 0.f};
+    float rs, rsb;
+    auto exps = [&]() __attribute__((always_inline)) {
+      const float mc = m * c;
+      float r2[2] = {0.f, 0.f}, rb2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < T::KS_PV; ++kk) {
-      const int h8 = (kk & 1) * 8;
+      for (int kk = 0; kk < T::KS_PV; ++kk) {
+        const int h8 = (kk & 1) * 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
-        rs[e & 1] += e0 + e1;
-        // The pair goes to dot2 directly: fed from an element of the packed
-        // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
-        bf16x2_t pe;
-        pe[0] = (__bf16)e0;
-        pe[1] = (__bf16)e1;
-        rsb[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rsb[e & 1], false);
-        pw[kk][e] = __builtin_bit_cast(uint32_t, pe);
+        for (int e = 0; e < 4; ++e) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
+          r2[e & 1] += e0 + e1;
+          // The pair goes to dot2 directly: fed from an element of the packed
+          // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
+          bf16x2_t pe;
+          pe[0] = (__bf16)e0;
+          pe[1] = (__bf16)e1;
+          rb2[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rb2[e & 1], false);
+          pw[kk][e] = __builtin_bit_cast(uint32_t, pe);
+        }
+      }
+      rs = r2[0] + r2[1];
+      rsb = rb2[0] + rb2[1];
+    };
+    exps();
+    if (__any(!(rs <= kSumBound))) {  // also taken for inf / NaN sums (first tile: m = -inf)
+      // row max: four independent chains, then across the two lane halves
+      float mx[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < T::NSUB; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[sub][r]);
+      const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+      // move the reference max only when some row outgrew it by 2^kRescaleLog2;
+      // the first tile holds key 0, visible to every row, so m is finite after it
+      if (__any((mt - m) * c > kRescaleLog2)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+        l *= alpha;
+        lb *= alpha;
+#pragma unroll
+        for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
+        m = m_new;
+        exps();
       }
     }
-    l += rs[0] + rs[1];
-    lb += rsb[0] + rsb[1];
+    l += rs;
+    lb += rsb;
   };
 
   // ---- matrix phase: Oᵀ += Vᵀ_j P̃ᵀ_j and Sᵀ_{j+1} = K_{j+1} Qᵀ, MFMAs interleaved ------
@@ -394,13 +414,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   auto batch_tiles = [&](int b) { return (b + 4 < n_tiles ? 1 : 0) + (b + 3 >= 0 && b + 3 < n_tiles ? 1 : 0); };
   auto wait_batches = [&](int pending) {  // at most `pending` tiles of loads outstanding
     if (pending >= 4)
-      wait_vmcnt<4 * T::LOADS>();
+      wait_vmcnt<8 * T::LOADS>();
     else if (pending == 3)
-      wait_vmcnt<3 * T::LOADS>();
+      wait_vmcnt<6 * T::LOADS>();
     else if (pending == 2)
-      wait_vmcnt<2 * T::LOADS>();
+      wait_vmcnt<4 * T::LOADS>();
     else if (pending == 1)
-      wait_vmcnt<T::LOADS>();
+      wait_vmcnt<2 * T::LOADS>();
     else
       wait_vmcnt<0>();
   };
@@ -409,10 +429,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(P));
     if (b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(P + 3));
   };
+  if (grp == 1) {
 #pragma unroll
-  for (int b = -4; b < 0; ++b) {
-    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(b + 4));
-    if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(b + 3));
+    for (int b = -4; b < 0; ++b) {
+      if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(b + 4));
+      if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(b + 3));
+    }
   }
   wait_batches(batch_tiles(-3) + batch_tiles(-2) + batch_tiles(-1));
   // The Q loads were issued before the tile loads, so they are complete now;
@@ -435,15 +457,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       softmax(j, std::true_type{});
     else if (active(j))
       softmax(j, std::false_type{});
-    if (grp == 0) wait_batches(batch_tiles(j - 2) + batch_tiles(j - 1));
+    if (grp == 1) wait_batches(batch_tiles(j - 1) + batch_tiles(j));
+
     block_barrier();
     // X(j)
     if (CLEAN)
       matrix_clean(vb(P), kb(P + 1));
     else
       matrix(vb(P), kb(P + 1), active(j), j + 1 < n_tiles && active(j + 1));
-    if (grp == 0) issue_batch(j, phase);
-    if (grp == 1) wait_batches(batch_tiles(j - 1) + batch_tiles(j));
     block_barrier();
   };
   using I0 = std::integral_constant<int, 0>;

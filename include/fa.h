@@ -65,7 +65,10 @@ typedef enum fa_status {
  *             must be positive and finite (FA_ERR_VALUE otherwise).
  *   causal  : nonzero masks key j from query i when j > i (square, top-left
  *             aligned: query i sees keys 0..i).
- * Any N ≥ 1 is accepted; N need not be a multiple of a tile. */
+ * Any N ≥ 1 is accepted; N need not be a multiple of a tile.  Inputs must be
+ * finite, and |v| < 2^56: the kernel keeps the unnormalised softmax weights
+ * below 2^48 (a stale running max is only moved when a logit outgrows it by
+ * that much), so the fp32 accumulation of weight·v cannot overflow. */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 

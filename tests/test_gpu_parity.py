@@ -169,6 +169,22 @@ def test_large_logits_are_stable():
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_running_max_grows_past_the_rescale_threshold(d):
+    """Key rows scaled up along the sequence (×1 … ×40): logits keep growing far
+    beyond the first tile's maximum, so the running max is moved (and the
+    accumulator rescaled) many times, also on tiles that cross the diagonal."""
+    w = W[2].with_(B=1, H=2, N=1000, d=d, boost_frac=0.0, wid=85 + d)
+    q, k, v = synth.make_prefill(w)
+    ramp = torch.linspace(1.0, 40.0, w.N).view(1, 1, -1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    for causal in (False, True):
+        o, lse = _run_fwd(q, k, v, w.scale, causal)
+        ro, rl = attention_ref(q, k, v, w.scale, causal)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        _check(f"growing logits d={d} causal={causal}", o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_decode_split_extremes(d):
     """num_splits = 1, = Lkv (one key each), uneven, and the default."""
     w = W[4].with_(B=2, H=3, lkv=1000, d=d, wid=90 + d)
