@@ -212,12 +212,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   const size_t base = (size_t)bh * N * D;
   const int grp = wave_u >> 2;  // wavefronts w and w+4 share a SIMD and alternate phases
 
-  // Direct global->LDS loads: wavefront `wave`, load i fills LDS chunk slots
-  // (i*8 + wave)*64 + lane of the tile; the slot's (row, swizzled chunk) names
-  // the global chunk this lane fetches.  Load i covers rows r0 + i*RPL, and
-  // both swizzles repeat with that period, so load i is load 0 shifted by
-  // i*RPL rows.  Rows past N lie past the head's bytes and read as zero (their
-  // logits are masked).
+  // Direct global->LDS loads, issued by the four wavefronts of group 1:
+  // wavefront w (w & 3 = u), load i fills LDS chunk slots (i*4 + u)*64 + lane
+  // of the tile; the slot's (row, swizzled chunk) names the global chunk this
+  // lane fetches.  Load i covers rows r0 + i*RPL, and both swizzles repeat
+  // with that period, so load i is load 0 shifted by i*RPL rows.  Rows past N
+  // lie past the head's bytes and read as zero (their logits are masked).
   constexpr int RPL = (kFwdWaves / 2) * 64 / T::CH;  // rows covered by one load across group 1
   const int r0 = ((wave & 3) * 64 + lane) / T::CH;
   const int cpos = lane % T::CH;
@@ -404,11 +404,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   // Sᵀ_{j+1} = K_{j+1} Qᵀ.  Group 1 (wavefronts 4-7) starts one barrier later
   // than group 0, so the two wavefronts of a SIMD are always in opposite
   // phases: one feeds the matrix core while the other runs the softmax.
-  // Loads go by the global phase T (group 0's phase index; group 1's plus one).
-  // Batch b (K_{b+4}, V_{b+3}) is issued at T = 2b+2, into the buffers that
-  // K_b and V_{b-1} left at T = 2b+1, and must be complete when T = 2b+8
-  // begins (group 0's X(b+3)): group 0 waits for it at the end of Y(b+3),
-  // group 1 at the end of X(b+2).
+  // Only group 1 loads, and only in its softmax phases, so the matrix phases
+  // never issue or wait for a load.  With T the global phase (group 0's
+  // phase index; group 1's plus one), batch b (K_{b+4}, V_{b+3}) is issued at
+  // the start of group 1's Y(b), T = 2b+2, into the buffers that K_b and
+  // V_{b-1} left at T = 2b+1; group 1 waits for it at the end of its Y(b+2),
+  // T = 2b+6, before group 0's X(b+3) reads it at T = 2b+8.
   auto kb = [&](int j) { return kbufs[j & 3]; };
   auto vb = [&](int j) { return vbufs[j & 3]; };
   auto batch_tiles = [&](int b) { return (b + 4 < n_tiles ? 1 : 0) + (b + 3 >= 0 && b + 3 < n_tiles ? 1 : 0); };
@@ -458,7 +459,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     else if (active(j))
       softmax(j, std::false_type{});
     if (grp == 1) wait_batches(batch_tiles(j - 1) + batch_tiles(j));
-
     block_barrier();
     // X(j)
     if (CLEAN)
