@@ -95,6 +95,22 @@ def test_long_noncausal_sampled_rows():
     _check(w.name + " (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
 
 
+@pytest.mark.parametrize("n,causal,d", [(4097, True, 128), (4352, True, 64), (4352, False, 64)])
+def test_many_blocks_ragged(n, causal, d):
+    """H = 32 with ragged N: more than two query blocks per compute unit and an odd
+    block count per head; sampled rows cover the block edges and the last row."""
+    w = W[2].with_(B=1, H=32, N=n, d=d, causal=causal, boost_frac=0.0, wid=60 + d + (1 if causal else 0))
+    _say("[case] many blocks, ragged N", n, causal, d)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, causal)
+    rng = np.random.default_rng(n + d)
+    edges = [r for b in range(0, n, 256) for r in (b, b + 31, b + 32, b + 255) if r < n]
+    rows = np.unique(np.concatenate([edges, [n - 1], rng.choice(n, 120, replace=False)]))
+    heads = [0, 13, 31]
+    ro, rl = attention_ref(q[:, heads], k[:, heads], v[:, heads], w.scale, causal, rows=rows)
+    _check(f"H32 N={n} causal={causal} d={d} (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
+
+
 def test_decode_full_size_sampled_heads():
     """B16 H32 Lkv 32768 d128, 64 splits; the oracle recomputes 8 heads unsplit."""
     w = W[4]
