@@ -11,6 +11,8 @@ Each call is also timed with HIP events recorded on the stream it runs on
   * decode.value     GB/s of algorithmic bytes (K, V once; q in; O, LSE out)
   * roofline         fa_fwd against the bf16 dense MFMA peak (2.5166 PFLOP/s)
   * roofline_decode  the decode pair against the HBM peak (8 TB/s)
+  * decode_gqa       grouped-query decode (B16, 32 query heads over 8 K/V heads,
+                     Lkv 32768, d128), timed on its own after the step
   * cpu_baseline     the fp64 oracle on a bounded sample of the same workload,
                      on this host's cores (rank 0, N=1 only)
 Prints one JSON line.
@@ -36,9 +38,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "copy"], default="all",
-                    help="time one call kind only (for counter collection); 'copy' times a plain "
-                         "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "copy"], default="all",
+                    help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
+                         "decode measured after the step; 'copy' times a plain 1 GiB device-to-device "
+                         "copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -54,6 +57,7 @@ def parse():
 TRAFFIC_KERNELS = {
     "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_internal.h"]),
     "decode": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
+    "gqa": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
     "copy": (["copyBuffer"], []),
 }
 
@@ -101,7 +105,9 @@ def make_traffic(args):
     f_w = gib_kib / per_launch("copy", "WRITE_SIZE")
     out = {"method": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by a 1 GiB copy",
            "fetch_scale": round(f_r, 4), "write_scale": round(f_w, 4)}
-    for kind in ("fwd", "decode"):
+    for kind in ("fwd", "decode", "gqa"):
+        if not os.path.isdir(os.path.join(args.make_traffic, f"FETCH_SIZE_{kind}")):
+            continue
         fk, wk = per_launch(kind, "FETCH_SIZE"), per_launch(kind, "WRITE_SIZE")
         out[kind] = {"bytes_per_launch": round((fk * f_r + wk * f_w) * 1024.0),
                      "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
@@ -182,6 +188,34 @@ def copy_reference(torch, dev, args):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
                       "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
     return 0
+
+
+def time_gqa(torch, fa, synth, dev, args, traffic):
+    """The grouped-query decode (32 query heads over 8 K/V heads, full lengths), timed
+    on its own after the step: W warm-up calls, then K calls, each between HIP events."""
+    wg = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s64"]
+    print(f"[bench] generating inputs: {wg.name}", file=sys.stderr, flush=True)
+    qg = synth.make_decode_q(wg).to(dev)
+    kg, vg = synth.make_decode_kv(wg, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(wg.B, wg.H, wg.d, wg.num_splits), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        fa.fa_decode_gqa(qg, kg, vg, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record()
+        fa.fa_decode_gqa(qg, kg, vg, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    avg = sum(ms) / len(ms)
+    gbytes = synth.decode_bytes(wg)
+    gbs = gbytes / (avg * 1e-3) / 1e9
+    del kg, vg
+    return {"workload": wg.name, "B": wg.B, "Hq": wg.H, "Hkv": wg.kv_heads, "Lkv": wg.lkv, "d": wg.d,
+            "num_splits": wg.num_splits, "value": round(gbs, 1), "unit": "GB/s", "ms": round(avg, 4),
+            "ms_min": round(min(ms), 4), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
 
 
 def main():
@@ -301,6 +335,8 @@ def main():
                                   "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_bytes(traffic, "decode"), "algorithmic_bytes": dbytes}
+    if args.only in ("all", "gqa"):
+        out["decode_gqa"] = time_gqa(torch, fa, synth, dev, args, traffic)
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)

@@ -8,6 +8,7 @@ library is missing or fails to load, the calls raise.
 
     fa_fwd(q, k, v, scale=None, causal=False)        -> (o, lse)
     fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
+    fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None) -> (o, lse)
     fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
     fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
     fa_fwd_tile_shape(d)                             -> (block_m, block_n)
@@ -51,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, vp, sz, vp]
+    lib.fa_decode_gqa.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_fwd_tile_pairs.argtypes = [i, i, i]
@@ -160,7 +163,7 @@ def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
-        num_splits = max(1, min(L, -(-1024 // (B * H)), max(1, L // 256)))
+        num_splits = default_splits(B * H, L)
     need = fa_decode_workspace_bytes(B, H, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -171,4 +174,59 @@ def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
                                   workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_decode")
+    return o, lse
+
+
+def default_splits(groups: int, L: int) -> int:
+    """Segments per (sequence, head group): about 1024 workgroups in all, at least
+    256 keys per segment, at most L segments."""
+    return max(1, min(L, -(-1024 // groups), max(1, L // 256)))
+
+
+def _group_width(g: int) -> int:
+    return 8 if g % 8 == 0 else 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+
+
+def fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None, workspace=None):
+    """Grouped-query split-KV decode: q bf16 [B, Hq, 1, d], k/v bf16 [B, Hkv, Lmax, d]
+    with Hq a multiple of Hkv (query head h reads K/V head h // (Hq // Hkv)).
+
+    ``seqlens`` (int32 [B] on the device, or None) gives each sequence's number of
+    keys; entries outside [1, Lmax] are clamped by the kernel.  Returns
+    (o bf16 [B, Hq, 1, d], lse fp32 [B, Hq]).  Runs on the current stream.
+    """
+    torch = _torch()
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    _check(v, "v", 4)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence, q has {one}")
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, L = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError(f"query heads {Hq} are not a multiple of K/V heads {Hkv}")
+    sl = None
+    if seqlens is not None:
+        if not isinstance(seqlens, torch.Tensor) or seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+            raise TypeError("seqlens must be an int32 tensor of shape [B]")
+        if seqlens.device != q.device or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be contiguous and on q's device")
+        sl = seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        g = Hq // Hkv
+        num_splits = default_splits(B * Hkv * (g // _group_width(g)), L)
+    need = fa_decode_workspace_bytes(B, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = load_library().fa_decode_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      B, Hq, Hkv, L, d, sl, float(scale), int(num_splits), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_gqa")
     return o, lse

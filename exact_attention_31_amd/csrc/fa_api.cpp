@@ -107,24 +107,32 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return o_bytes + parts * 4;
 }
 
-fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lkv,
-                    int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                        int Lmax, int d, const int* seqlens, float scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || Lkv < 1) return FA_ERR_SHAPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const size_t kv_elems = count4(B, H, Lkv, d);
-  if (kv_elems == 0 || (unsigned long long)B * H * num_splits > 0x7fffffffull) return FA_ERR_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.f) || num_splits < 1 || num_splits > Lkv) return FA_ERR_VALUE;
-  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  const size_t kv_elems = count4(B, Hkv, Lmax, d);
+  if (kv_elems == 0 || count4(B, Hq, 1, d) == 0 || (unsigned long long)B * Hq * num_splits > 0x7fffffffull)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f) || num_splits < 1 || num_splits > Lmax) return FA_ERR_VALUE;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
     return FA_ERR_ALIGN;
-  const size_t qb = (size_t)B * H * d * 2, kb = kv_elems * 2, lb = (size_t)B * H * 4;
+  const size_t qb = (size_t)B * Hq * d * 2, kb = kv_elems * 2, lb = (size_t)B * Hq * 4;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) || overlap(lse, lb, q, qb) ||
       overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(o, qb, lse, lb) ||
       overlap(workspace, need, q, qb) || overlap(workspace, need, k, kb) || overlap(workspace, need, v, kb) ||
       overlap(workspace, need, o, qb) || overlap(workspace, need, lse, lb))
     return FA_ERR_ALIAS;
+  if (seqlens) {
+    const size_t sb = (size_t)B * 4;
+    if (overlap(o, qb, seqlens, sb) || overlap(lse, lb, seqlens, sb) || overlap(workspace, need, seqlens, sb))
+      return FA_ERR_ALIAS;
+  }
 
   fa::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -133,14 +141,23 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.part_o = static_cast<float*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)B * H * num_splits * d * 4);
-  p.H = H;
-  p.L = Lkv;
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)B * Hq * num_splits * d * 4);
+  p.seqlens = seqlens;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.L = Lmax;
   p.S = num_splits;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   if (fa::launch_decode(p, B, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lkv,
+                    int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_decode_gqa(q, k, v, o, lse, B, H, H, Lkv, d, nullptr, scale, num_splits, workspace, workspace_bytes,
+                       stream);
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-// Split-KV decode for CDNA4 (gfx950): one query per (b, h) against Lkv keys.
+// Split-KV decode for CDNA4 (gfx950): one new query per (b, query head)
+// against the cached keys of its sequence.
 //
 // Decode has one query row per sequence, so a grid over (b, h) alone leaves
 // most compute units idle; the keys are therefore split into S segments, each
@@ -8,19 +9,30 @@
 // is associative and commutative ([15-779 L5] §4.4–4.5), so the split count
 // does not change the result beyond rounding.
 //
+// Grouped queries ([15-779 L5] §12, exercise 7): g = Hq/Hkv query heads share
+// one K/V head (g = 1: multi-head; Hkv = 1: multi-query).  A workgroup serves
+// GQ of the g query heads of its K/V head, so every K/V byte it streams feeds
+// GQ dot products and GQ accumulators: the arithmetic intensity rises by GQ.
+// Sequences may hold fewer keys than the cache's row count (per-sequence
+// lengths); each sequence's keys are split into its own S segments, and a
+// segment left empty (a sequence shorter than S) contributes weight 0.
+//
 // Pages cited: [15-779 L5] "第 5 讲 · 案例：Transformer、注意力与 FlashAttention".
 //
-// The work is a pure stream of K and V (one multiply-add per byte pair), so it
+// The work is a stream of K and V (a few multiply-adds per byte pair), so it
 // is bound by HBM bandwidth ([15-779 L5] §8.3): the kernel reads each key row
 // with 16-byte loads by d/8 adjacent lanes (a wavefront instruction covers
-// 1 KiB of contiguous cache), keeps eight such loads of K and eight of V in
-// flight per lane, and does the arithmetic in fp32 on the vector ALUs —
-// a matrix-core formulation would not help a matrix-vector product.
+// 1 KiB of contiguous cache), keeps several such loads of K and of V in
+// flight per lane, and does the arithmetic on the vector ALUs — q·k as
+// bf16-pair dot products (v_dot2_f32_bf16) summed across the d/8 lanes of a
+// row on the DPP lane network, P̃·v in fp32 — as a matrix-core formulation
+// would not help a matrix-vector product.
 //
 // Lane roles inside a wavefront: lane = slot·(d/8) + chunk; `chunk` selects 8
 // dims of the row, `slot` selects one of 64/(d/8) keys per instruction.  Each
-// slot keeps its own running (m, ℓ, o[8]) over the keys it sees; the slots,
-// then the 4 wavefronts, are merged with ⊕ at the end of the segment.
+// slot keeps its own running (m, ℓ, o[8]) per query over the keys it sees;
+// the slots, then the 4 wavefronts, are merged with ⊕ at the end of the
+// segment.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -36,10 +48,30 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kUnroll = 8;  // wavefront instructions of K (and of V) in flight per lane
+// wavefront instructions of K (and of V) in flight per lane: fewer when each
+// key feeds more queries (more registers per key, more arithmetic per byte)
+__host__ __device__ constexpr int dec_unroll(int gq) { return gq >= 8 ? 4 : 8; }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Σ over the `lanes` adjacent lanes (a power of two, at most 16, aligned) that
+// share a key row, left in every one of them: butterfly steps on the DPP lane
+// network (quad permutations, then mirrors within 8 and 16 lanes), each a
+// plain vector add with a permuted operand — no LDS crossbar round trip.
+template <int lanes>
+__device__ inline float row_sum(float t) {
+  t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+  if (lanes > 2)
+    t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, true)); // [2,3,0,1]
+  if (lanes > 4)
+    t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x141, 0xF, 0xF, true)); // half mirror
+  if (lanes > 8)
+    t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x140, 0xF, 0xF, true)); // mirror
+  return t;
+}
 
 __device__ inline uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
@@ -49,137 +81,165 @@ __device__ inline uint16_t to_bf16(float x) {
 // summary carries weight exactly 0 after the merge.
 __device__ inline float safe_mc(float m, float c) { return m == -INFINITY ? 0.f : m * c; }
 
-template <int D>
+template <int D, int GQ>
 __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPI = 64 / LPK;     // keys per wavefront instruction
   constexpr int STEP = kDecWaves * KPI;
+  constexpr int UNR = dec_unroll(GQ);
 
+  // workgroup -> (segment s, query group qg of K/V head (b, hk))
   const int s = blockIdx.x % p.S;   // consecutive workgroups walk one head's segments
-  const int bh = blockIdx.x / p.S;
+  const int rest = blockIdx.x / p.S;
+  const int n_qg = p.G / GQ;
+  const int qg = rest % n_qg;
+  const int bk = rest / n_qg;       // b·Hkv + hk
+  const int b = bk / p.Hkv;
+  const int hq0 = (bk % p.Hkv) * p.G + qg * GQ;  // first of the GQ query heads
+  const size_t bq0 = (size_t)b * p.Hq + hq0;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int chunk = lane % LPK;
   const int slot = lane / LPK;
-  const int k_begin = (int)(((long long)s * p.L) / p.S);
-  const int k_end = (int)(((long long)(s + 1) * p.L) / p.S);
+  int len = p.L;
+  if (p.seqlens) {
+    const int x = p.seqlens[b];
+    len = x < 1 ? 1 : (x > p.L ? p.L : x);
+  }
+  const int k_begin = (int)(((long long)s * len) / p.S);
+  const int k_end = (int)(((long long)(s + 1) * len) / p.S);
   const float c = p.scale_log2;
 
-  float qf[8];
-  {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.q + (size_t)bh * D + chunk * 8);
+  // q stays in bf16 pairs: q·k takes one v_dot2_f32_bf16 per pair of dims
+  uint32_t qw[GQ][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[2 * e] = bf_lo(w[e]);
-      qf[2 * e + 1] = bf_hi(w[e]);
-    }
+  for (int i = 0; i < GQ; ++i) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.q + (bq0 + i) * D + chunk * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qw[i][e] = w[e];
   }
-  const uint16_t* __restrict__ kb = p.k + (size_t)bh * p.L * D + chunk * 8;
-  const uint16_t* __restrict__ vb = p.v + (size_t)bh * p.L * D + chunk * 8;
+  const uint16_t* __restrict__ kb = p.k + (size_t)bk * p.L * D + chunk * 8;
+  const uint16_t* __restrict__ vb = p.v + (size_t)bk * p.L * D + chunk * 8;
 
-  float m = -INFINITY, l = 0.f;
-  float acc[8];
+  float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int i = 0; i < GQ; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  }
 
-  for (int k0 = k_begin; k0 < k_end; k0 += kUnroll * STEP) {
-    u32x4_t kr[kUnroll], vr[kUnroll];
-    int key[kUnroll];
+  for (int k0 = k_begin; k0 < k_end; k0 += UNR * STEP) {
+    u32x4_t kr[UNR], vr[UNR];
+    int key[UNR];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       key[u] = k0 + (u * kDecWaves + wave) * KPI + slot;
       kr[u] = key[u] < k_end ? *reinterpret_cast<const u32x4_t*>(kb + (size_t)key[u] * D) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < UNR; ++u)
       vr[u] = key[u] < k_end ? *reinterpret_cast<const u32x4_t*>(vb + (size_t)key[u] * D) : u32x4_t{0, 0, 0, 0};
 
-    float sc[kUnroll];
-    float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float t = 0.f;
+    for (int i = 0; i < GQ; ++i) {
+      float sc[UNR];
+      float bm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t = fmaf(qf[2 * e], bf_lo(kr[u][e]), t);
-        t = fmaf(qf[2 * e + 1], bf_hi(kr[u][e]), t);
+      for (int u = 0; u < UNR; ++u) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[i][e]),
+                                              __builtin_bit_cast(bf16x2_t, (uint32_t)kr[u][e]), t, false);
+        t = row_sum<LPK>(t);
+        sc[u] = key[u] < k_end ? t : -INFINITY;
+        bm = fmaxf(bm, sc[u]);
       }
+      const float m_new = fmaxf(m[i], bm);
+      const float mc = safe_mc(m_new, c);
+      const float alpha = __builtin_amdgcn_exp2f(m[i] * c - mc);
+      l[i] *= alpha;
 #pragma unroll
-      for (int off = 1; off < LPK; off <<= 1) t += __shfl_xor(t, off);
-      sc[u] = key[u] < k_end ? t : -INFINITY;
-      bm = fmaxf(bm, sc[u]);
-    }
-    const float m_new = fmaxf(m, bm);
-    const float mc = safe_mc(m_new, c);
-    const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
-    l *= alpha;
+      for (int e = 0; e < 8; ++e) acc[i][e] *= alpha;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      for (int u = 0; u < UNR; ++u) {
+        const float pu = __builtin_amdgcn_exp2f(fmaf(sc[u], c, -mc));
+        l[i] += pu;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float pu = __builtin_amdgcn_exp2f(fmaf(sc[u], c, -mc));
-      l += pu;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(pu, bf_lo(vr[u][e]), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(pu, bf_hi(vr[u][e]), acc[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          acc[i][2 * e] = fmaf(pu, bf_lo(vr[u][e]), acc[i][2 * e]);
+          acc[i][2 * e + 1] = fmaf(pu, bf_hi(vr[u][e]), acc[i][2 * e + 1]);
+        }
       }
+      m[i] = m_new;
     }
-    m = m_new;
   }
 
   // ⊕-merge the slots of this wavefront (lanes that share a chunk).
 #pragma unroll
-  for (int off = LPK; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float l2 = __shfl_xor(l, off);
-    const float mm = fmaxf(m, m2);
-    const float mmc = safe_mc(mm, c);
-    const float fa = __builtin_amdgcn_exp2f(m * c - mmc);
-    const float fb = __builtin_amdgcn_exp2f(m2 * c - mmc);
-    l = l * fa + l2 * fb;
+  for (int i = 0; i < GQ; ++i) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float a2 = __shfl_xor(acc[e], off);
-      acc[e] = acc[e] * fa + a2 * fb;
+    for (int off = LPK; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m[i], off);
+      const float l2 = __shfl_xor(l[i], off);
+      const float mm = fmaxf(m[i], m2);
+      const float mmc = safe_mc(mm, c);
+      const float fa = __builtin_amdgcn_exp2f(m[i] * c - mmc);
+      const float fb = __builtin_amdgcn_exp2f(m2 * c - mmc);
+      l[i] = l[i] * fa + l2 * fb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a2 = __shfl_xor(acc[i][e], off);
+        acc[i][e] = acc[i][e] * fa + a2 * fb;
+      }
+      m[i] = mm;
     }
-    m = mm;
   }
 
-  // ⊕-merge the wavefronts through LDS and write the segment's (O_s, LSE_s).
-  __shared__ float sm_m[kDecWaves], sm_l[kDecWaves];
-  __shared__ float sm_o[kDecWaves][D];
+  // ⊕-merge the wavefronts through LDS and write the segment's (O_s, LSE_s);
+  // an empty segment (a sequence shorter than S) writes O_s = 0, LSE_s = -inf.
+  __shared__ float sm_m[GQ][kDecWaves], sm_l[GQ][kDecWaves];
+  __shared__ float sm_o[GQ][kDecWaves][D];
   if (slot == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm_o[wave][chunk * 8 + e] = acc[e];
-    if (chunk == 0) {
-      sm_m[wave] = m;
-      sm_l[wave] = l;
+    for (int i = 0; i < GQ; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_o[i][wave][chunk * 8 + e] = acc[i][e];
+      if (chunk == 0) {
+        sm_m[i][wave] = m[i];
+        sm_l[i][wave] = l[i];
+      }
     }
   }
   __syncthreads();
-  if (tid < D) {
-    float M = sm_m[0];
+  for (int x = tid; x < GQ * D; x += kDecThreads) {
+    const int i = x / D, dd = x % D;
+    float M = sm_m[i][0];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, sm_m[w]);
+    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, sm_m[i][w]);
     const float Mc = safe_mc(M, c);
     float L = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm_m[w] * c - Mc);
-      L = fmaf(sm_l[w], f, L);
-      o = fmaf(sm_o[w][tid], f, o);
+      const float f = __builtin_amdgcn_exp2f(sm_m[i][w] * c - Mc);
+      L = fmaf(sm_l[i][w], f, L);
+      o = fmaf(sm_o[i][w][dd], f, o);
     }
-    const size_t part = (size_t)bh * p.S + s;
-    p.part_o[part * D + tid] = o / L;
-    if (tid == 0) p.part_lse[part] = M * p.scale + __builtin_amdgcn_logf(L) * 0.69314718055994531f;
+    const size_t part = (bq0 + i) * p.S + s;
+    const bool empty = !(L > 0.f);
+    p.part_o[part * D + dd] = empty ? 0.f : o / L;
+    if (dd == 0) p.part_lse[part] = empty ? -INFINITY : M * p.scale + __builtin_amdgcn_logf(L) * 0.69314718055994531f;
   }
 }
 
 // O = Σ_s w_s O_s / Σ_s w_s and LSE = M + ln Σ_s w_s with w_s = exp(LSE_s − M),
-// M = max_s LSE_s: the ⊕ merge written on normalised partials.  One
-// workgroup per (b, h): the max over segments is a block reduction, then
+// M = max_s LSE_s: the ⊕ merge written on normalised partials (an empty
+// segment has LSE_s = -inf, weight 0, and O_s = 0).  One workgroup per
+// (b, query head): the max over segments is a block reduction, then
 // groups of threads take interleaved segments (16-byte loads of O_s, d/4
 // threads per segment) and the groups' partial sums meet in LDS.
 constexpr int kCombThreads = 256;
@@ -193,7 +253,7 @@ __global__ __launch_bounds__(kCombThreads) void fa_decode_combine_kernel(DecodeP
   __shared__ f32x4_t part[G][C4];
   __shared__ float wsum[G];
 
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x;  // b·Hq + query head
   const int t = threadIdx.x;
   const float* __restrict__ pl = p.part_lse + (size_t)bh * p.S;
   const f32x4_t* __restrict__ po = reinterpret_cast<const f32x4_t*>(p.part_o + (size_t)bh * p.S * D);
@@ -235,20 +295,30 @@ __global__ __launch_bounds__(kCombThreads) void fa_decode_combine_kernel(DecodeP
   }
 }
 
-template <int D>
+template <int D, int GQ>
 hipError_t launch_decode_t(const DecodeParams& p, int B, hipStream_t stream) {
-  const int BH = B * p.H;
-  hipLaunchKernelGGL(fa_decode_split_kernel<D>, dim3(BH * p.S), dim3(kDecThreads), 0, stream, p);
+  const long long groups = (long long)B * p.Hkv * (p.G / GQ);
+  hipLaunchKernelGGL((fa_decode_split_kernel<D, GQ>), dim3((unsigned)(groups * p.S)), dim3(kDecThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fa_decode_combine_kernel<D>, dim3(BH), dim3(kCombThreads), 0, stream, p);
+  hipLaunchKernelGGL(fa_decode_combine_kernel<D>, dim3(B * p.Hq), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeParams& p, int B, hipStream_t stream) {
+  switch (decode_group_width(p.G)) {
+    case 8: return launch_decode_t<D, 8>(p, B, stream);
+    case 4: return launch_decode_t<D, 4>(p, B, stream);
+    case 2: return launch_decode_t<D, 2>(p, B, stream);
+    default: return launch_decode_t<D, 1>(p, B, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream) {
-  return d == 64 ? launch_decode_t<64>(p, B, stream) : launch_decode_t<128>(p, B, stream);
+  return d == 64 ? launch_decode_d<64>(p, B, stream) : launch_decode_d<128>(p, B, stream);
 }
 
 }  // namespace fa

@@ -47,14 +47,21 @@ struct DecodeParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  float* part_o;     // [BH, S, d] fp32
-  float* part_lse;   // [BH, S]    fp32
-  int H;
-  int L;
+  float* part_o;     // [B, Hq, S, d] fp32
+  float* part_lse;   // [B, Hq, S]    fp32
+  const int* seqlens;  // [B] keys per sequence, or null: all L
+  int Hq;            // query heads
+  int Hkv;           // key/value heads; query head h reads K/V head h / G
+  int G;             // Hq / Hkv
+  int L;             // key rows per (b, K/V head) in the cache
   int S;
   float scale;
   float scale_log2;
 };
+
+// Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
+// divides the group size g = Hq / Hkv.
+__host__ __device__ inline int decode_group_width(int g) { return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream);

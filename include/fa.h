@@ -13,7 +13,9 @@
  *              diagonal follows [15-779 L5] §6.2.
  *   fa_decode  decode: one new query per sequence against Lkv cached keys, with
  *              the keys split into segments whose partial results are merged by
- *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5).
+ *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5);
+ *              fa_decode_gqa adds grouped query heads (several query heads per
+ *              cached K/V head) and per-sequence key counts.
  *
  * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
  * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
@@ -94,6 +96,30 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Lkv, int d, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped-query split-KV decode with per-sequence key counts.
+ *   q, o    : bf16 [B, Hq, 1, d].
+ *   k, v    : bf16 [B, Hkv, Lmax, d], contiguous per (b, K/V head).  Hq must
+ *             be a multiple of Hkv: with g = Hq/Hkv, query head h attends
+ *             with K/V head ⌊h/g⌋ (g query heads share one cached head,
+ *             [15-779 L5] §12 exercise 7; g = 1 is multi-head, Hkv = 1
+ *             multi-query).
+ *   seqlens : device int32 [B] (4-byte aligned) or NULL.  Sequence b attends
+ *             to its keys 0 .. seqlens[b]-1; entries outside [1, Lmax] are
+ *             clamped into it (the device reads them: no host check is
+ *             possible).  NULL: every sequence has Lmax keys.
+ *   lse     : fp32 [B, Hq].
+ *   num_splits : 1 ≤ S ≤ Lmax.  Sequence b's keys are split into segments
+ *             [⌊s·len_b/S⌋, ⌊(s+1)·len_b/S⌋); a segment left empty by a
+ *             short sequence contributes nothing.
+ *   workspace : at least fa_decode_workspace_bytes(B, Hq, d, num_splits)
+ *             bytes, otherwise as for fa_decode.
+ * Other arguments, errors and stream behaviour as for fa_decode, which is
+ * this call with Hq = Hkv = H and seqlens = NULL. */
+fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Lmax, int d, const int* seqlens,
+                        float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
  * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not

@@ -25,6 +25,7 @@ from .ref import (
     safe_softmax,
     attention_ref,
     decode_ref,
+    decode_gqa_ref,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode
 
@@ -33,6 +34,7 @@ __all__ = [
     "safe_softmax",
     "attention_ref",
     "decode_ref",
+    "decode_gqa_ref",
     "bf16_half_ulp",
     "o_excess",
     "check_prefill",

@@ -123,3 +123,38 @@ def decode_ref(q, k, v, scale):
             o[b, h] = (e / l) @ v[b, h]
             lse[b, h] = m + np.log(l)
     return o, lse
+
+
+def decode_gqa_ref(q, k, v, scale, seqlens=None):
+    """Grouped-query decode with per-sequence key counts.
+
+    q: [B, Hq, d] or [B, Hq, 1, d]; k, v: [B, Hkv, Lmax, d] with Hq = g·Hkv.
+    Query head h attends with K/V head h // g — g query heads share one cached
+    head ([15-779 L5] §12, exercise 7) — to keys 0 .. seqlens[b]-1 of
+    sequence b (all Lmax when seqlens is None).  The same definition as
+    decode_ref, on the selected keys.  Returns (O [B, Hq, d], LSE [B, Hq]).
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    B, Hq, _ = q.shape
+    Hkv, Lmax = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0, "query heads must be a multiple of K/V heads"
+    g = Hq // Hkv
+    lens = [Lmax] * B if seqlens is None else [int(x) for x in np.asarray(seqlens)]
+    o = np.empty((B, Hq, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    for b in range(B):
+        n = lens[b]
+        assert 1 <= n <= Lmax, "each sequence holds between 1 and Lmax keys"
+        for h in range(Hq):
+            kh = h // g
+            s = scale * (k[b, kh, :n] @ q[b, h])     # [n] logits
+            m = s.max()
+            e = np.exp(s - m)
+            l = e.sum()
+            o[b, h] = (e / l) @ v[b, kh, :n]
+            lse[b, h] = m + np.log(l)
+    return o, lse

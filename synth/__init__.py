@@ -43,6 +43,11 @@ class Workload:
     boost_frac: float = 0.0
     boost: float = 1.0
     wid: int = 0         # seed namespace
+    hkv: int = 0         # decode: key/value heads (0: as many as query heads)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -63,9 +68,15 @@ WORKLOADS = [
     Workload("decode_b16h32_lkv32768_d128_s64", "decode", 16, 32, 1, 128, False,
              lkv=32768, num_splits=64, wid=5),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Grouped-query decode (Llama-3-8B's 32 query heads over 8 K/V heads), the
+# widening of the decode workload above to shared K/V heads.
+EXTRA_WORKLOADS = [
+    Workload("decode_gqa_b16hq32hkv8_lkv32768_d128_s64", "decode", 16, 32, 1, 128, False,
+             lkv=32768, num_splits=64, wid=6, hkv=8),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
-_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3}
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3, "seqlens": 4}
 
 
 def seed_for(w: Workload, tensor: str, b: int, h: int) -> int:
@@ -122,13 +133,25 @@ def make_decode_q(w: Workload) -> torch.Tensor:
 
 
 def make_decode_kv(w: Workload, device="cpu"):
-    """Decode K, V [B, H, Lkv, d] bf16, drawn on ``device`` one sequence (all heads) at a time."""
-    k = torch.empty((w.B, w.H, w.lkv, w.d), dtype=torch.bfloat16, device=device)
+    """Decode K, V [B, Hkv, Lkv, d] bf16, drawn on ``device`` one sequence (all heads) at a time."""
+    k = torch.empty((w.B, w.kv_heads, w.lkv, w.d), dtype=torch.bfloat16, device=device)
     v = torch.empty_like(k)
     for b in range(w.B):
-        k[b] = randn_bf16(seed_for(w, "k", b, 0), (w.H, w.lkv, w.d), device)
-        v[b] = randn_bf16(seed_for(w, "v", b, 0), (w.H, w.lkv, w.d), device)
+        k[b] = randn_bf16(seed_for(w, "k", b, 0), (w.kv_heads, w.lkv, w.d), device)
+        v[b] = randn_bf16(seed_for(w, "v", b, 0), (w.kv_heads, w.lkv, w.d), device)
     return k, v
+
+
+def make_seqlens(w: Workload) -> torch.Tensor:
+    """Per-sequence key counts for a ragged decode batch: int32 [B], uniform on
+    [1, Lkv] from a seeded generator, with the first sequence at the full Lkv
+    and the second at a single key (CPU; move to the device to use)."""
+    g = _gen(seed_for(w, "seqlens", 0, 0))
+    lens = torch.randint(1, w.lkv + 1, (w.B,), generator=g, dtype=torch.int64)
+    lens[0] = w.lkv
+    if w.B > 1:
+        lens[1] = 1
+    return lens.to(torch.int32)
 
 
 def prefill_flops(w: Workload) -> float:
@@ -137,9 +160,11 @@ def prefill_flops(w: Workload) -> float:
     return f / 2 if w.causal else f
 
 
-def decode_bytes(w: Workload) -> float:
-    """Algorithmic bytes of one decode call: K and V once, q in, O out (bf16), LSE out (fp32)."""
-    return float(w.B * w.H * (2 * w.lkv * w.d * 2 + 2 * w.d * 2 + 4))
+def decode_bytes(w: Workload, seqlens=None) -> float:
+    """Algorithmic bytes of one decode call: the visible K and V rows once per
+    K/V head, q in, O out (bf16), LSE out (fp32)."""
+    keys = w.B * w.lkv if seqlens is None else int(sum(int(x) for x in seqlens))
+    return float(keys * w.kv_heads * 2 * w.d * 2 + w.B * w.H * (2 * w.d * 2 + 4))
 
 
 def prefill_bytes(w: Workload) -> float:

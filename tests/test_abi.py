@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for want in ("fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+    for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
                  "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version"):
         assert want in names
 
@@ -91,6 +91,24 @@ def test_decode_argument_checks():
     assert _dec(ws=P[0]) == 8            # workspace on top of q
     assert _lib().fa_decode_workspace_bytes(0, 1, 64, 4) == 0
     assert _lib().fa_decode_workspace_bytes(1, 1, 80, 4) == 0
+
+
+def _gqa(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, Hq=4, Hkv=2, L=16, d=64, seqlens=None, scale=0.125, S=4,
+         ws=P[5], wsb=1 << 20):
+    return _lib().fa_decode_gqa(q, k, v, o, lse, B, Hq, Hkv, L, d, seqlens, ctypes.c_float(scale), S, ws, wsb, None)
+
+
+def test_decode_gqa_argument_checks():
+    assert _gqa(k=None) == 1
+    assert _gqa(Hq=6, Hkv=4) == 2          # query heads not a multiple of K/V heads
+    assert _gqa(Hkv=0) == 2 and _gqa(L=0) == 2
+    assert _gqa(d=32) == 3
+    assert _gqa(S=17) == 5 and _gqa(scale=0.0) == 5
+    assert _gqa(ws=None) == 6
+    need = _lib().fa_decode_workspace_bytes(1, 4, 64, 4)   # sized by the query heads
+    assert _gqa(wsb=need - 1) == 6
+    assert _gqa(seqlens=ctypes.c_void_p(0x50000002)) == 4  # int32 lengths must be 4-byte aligned
+    assert _gqa(seqlens=P[3]) == 8          # lengths inside the output
 
 
 def test_tile_shape():

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 import exact_attention_31_amd as fa
 import synth
-from oracle import attention_ref, decode_ref, check_prefill
+from oracle import attention_ref, decode_gqa_ref, decode_ref, check_prefill
 from oracle.compare import bf16_half_ulp
 
 pytestmark = pytest.mark.gpu
@@ -198,6 +198,71 @@ def test_running_max_grows_past_the_rescale_threshold(d):
         ro, rl = attention_ref(q, k, v, w.scale, causal)
         assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
         _check(f"growing logits d={d} causal={causal}", o, lse, ro, rl)
+
+
+# ----------------------------------------------------------------------------
+# grouped-query decode with per-sequence key counts
+
+
+def _gqa_case(B, Hq, Hkv, L, d, wid):
+    w = W[4].with_(B=B, H=Hq, hkv=Hkv, lkv=L, d=d, wid=wid)
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w, device="cuda")
+    return w, q, k, v
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,ragged,S", [
+    (2, 8, 8, 700, 128, False, 5),      # g = 1: multi-head
+    (3, 16, 4, 1000, 128, True, 7),     # g = 4
+    (2, 16, 2, 513, 64, True, 3),       # g = 8
+    (2, 32, 1, 300, 128, True, 64),     # multi-query, g = 32: four groups of 8; empty segments
+    (2, 6, 2, 257, 64, True, 1),        # g = 3: one query head per workgroup
+    (1, 12, 4, 2000, 128, False, 2000), # one key per segment
+])
+def test_decode_gqa(B, Hq, Hkv, L, d, ragged, S):
+    w, q, k, v = _gqa_case(B, Hq, Hkv, L, d, wid=140 + Hq + Hkv + d)
+    lens = synth.make_seqlens(w) if ragged else None
+    _say("[case] decode gqa", B, Hq, Hkv, L, d, None if lens is None else lens.tolist(), S)
+    o, lse = fa.fa_decode_gqa(q.cuda(), k, v, seqlens=None if lens is None else lens.cuda(), scale=w.scale,
+                              num_splits=S)
+    torch.cuda.synchronize()
+    ro, rl = decode_gqa_ref(q.float(), k.cpu(), v.cpu(), w.scale, seqlens=None if lens is None else lens.numpy())
+    _check(f"decode gqa B{B} Hq{Hq} Hkv{Hkv} L{L} d{d} S{S}", o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(),
+           ro, rl)
+
+
+def test_decode_is_decode_gqa_with_one_query_per_kv_head():
+    w, q, k, v = _gqa_case(2, 4, 4, 900, 128, wid=150)
+    o1, l1 = fa.fa_decode(q.cuda(), k, v, scale=w.scale, num_splits=9)
+    o2, l2 = fa.fa_decode_gqa(q.cuda(), k, v, scale=w.scale, num_splits=9)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_gqa_full_size_sampled_heads():
+    """B16 Hq32 Hkv8 Lmax 32768 d128, 64 splits, ragged lengths (one full, one of a
+    single key); the oracle recomputes 8 query heads of 4 sequences."""
+    w = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s64"]
+    _say("[case] workload", w.name, "(ragged lengths)")
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w, device="cuda")
+    lens = synth.make_seqlens(w)
+    o, lse = fa.fa_decode_gqa(q.cuda(), k, v, seqlens=lens.cuda(), scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    g = w.H // w.kv_heads
+    for b in (0, 1, 5, 15):
+        heads = [0, 3, 4, 13, 17, 22, 30, 31]
+        kh = sorted({h // g for h in heads})
+        kb, vb = k[b:b + 1, kh].cpu(), v[b:b + 1, kh].cpu()
+        remap = {x: i for i, x in enumerate(kh)}
+        # the oracle sees these query heads against their own K/V heads (g = 1 after selection)
+        qsel = q[b:b + 1, heads]
+        kq = torch.stack([kb[0, remap[h // g]] for h in heads])[None]
+        vq = torch.stack([vb[0, remap[h // g]] for h in heads])[None]
+        ro, rl = decode_gqa_ref(qsel.float(), kq, vq, w.scale, seqlens=lens[b:b + 1].numpy())
+        _check(f"{w.name} b={b} len={int(lens[b])}", o[b:b + 1, heads].float().cpu().numpy()[:, :, 0],
+               lse[b:b + 1, heads].cpu().numpy(), ro, rl)
+    del k, v
 
 
 @pytest.mark.parametrize("d", [64, 128])

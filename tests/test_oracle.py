@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import scipy.special
 
-from oracle import attention_ref, decode_ref, safe_softmax, scores
+from oracle import attention_ref, decode_gqa_ref, decode_ref, safe_softmax, scores
 from oracle.compare import bf16_half_ulp, bf16_rne, check_prefill
 import _method_fp64 as M
 
@@ -317,6 +317,69 @@ def test_decode_split_merge_equals_decode_ref():
             acc = M.merge_mlo(acc, p)
         np.testing.assert_allclose(acc[2] / acc[1], o[0, 0], rtol=0, atol=1e-13)
         assert abs(acc[0] + math.log(acc[1]) - lse[0, 0]) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# grouped-query decode with per-sequence key counts
+
+
+def test_decode_gqa_equals_decode_on_repeated_kv_heads():
+    """Query head h reads K/V head h // g: the same as plain decode on K/V whose
+    heads are repeated g times in a row (and not h % Hkv, which a transposed
+    grouping would give)."""
+    rng = np.random.default_rng(31)
+    B, Hkv, g, L, d = 2, 3, 4, 50, 16
+    q = rng.standard_normal((B, Hkv * g, 1, d))
+    k, v = rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    o, lse = decode_gqa_ref(q, k, v, 0.3)
+    ro, rl = decode_ref(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), 0.3)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-14)
+    wrong = decode_ref(q, np.tile(k, (1, g, 1, 1)), np.tile(v, (1, g, 1, 1)), 0.3)[0]
+    assert np.abs(o - wrong).max() > 1e-3
+
+
+def test_decode_gqa_seqlens_truncate_the_cache():
+    rng = np.random.default_rng(32)
+    B, Hkv, g, L, d = 3, 2, 2, 40, 8
+    q = rng.standard_normal((B, Hkv * g, d))
+    k, v = rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    lens = np.array([1, 17, 40])
+    o, lse = decode_gqa_ref(q, k, v, 0.5, seqlens=lens)
+    for b, n in enumerate(lens):
+        ro, rl = decode_ref(q[b:b + 1], np.repeat(k[b:b + 1, :, :n], g, axis=1),
+                            np.repeat(v[b:b + 1, :, :n], g, axis=1), 0.5)
+        np.testing.assert_allclose(o[b], ro[0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[b], rl[0], rtol=0, atol=1e-14)
+    # one key: the weight is exactly 1 on it
+    np.testing.assert_array_equal(o[0], np.repeat(v[0, :, 0], g, axis=0))
+
+
+def test_decode_gqa_zero_query_is_the_mean_of_the_visible_values():
+    """q = 0: every logit is 0, so O is the plain mean of the first len_b value rows
+    and LSE = ln len_b (closed form)."""
+    rng = np.random.default_rng(33)
+    B, Hkv, g, L, d = 2, 2, 3, 30, 4
+    v = rng.standard_normal((B, Hkv, L, d))
+    lens = np.array([7, 30])
+    o, lse = decode_gqa_ref(np.zeros((B, Hkv * g, d)), rng.standard_normal((B, Hkv, L, d)), v, 1.0, seqlens=lens)
+    for b, n in enumerate(lens):
+        for h in range(Hkv * g):
+            np.testing.assert_allclose(o[b, h], v[b, h // g, :n].mean(axis=0), rtol=0, atol=1e-14)
+            assert abs(lse[b, h] - math.log(n)) < 1e-14
+
+
+def test_decode_gqa_matches_decimal_bruteforce():
+    rng = np.random.default_rng(34)
+    B, Hkv, g, L, d = 1, 2, 2, 6, 5
+    q = rng.standard_normal((B, Hkv * g, d))
+    k, v = rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    lens = np.array([4])
+    o, lse = decode_gqa_ref(q, k, v, 0.4, seqlens=lens)
+    for h in range(Hkv * g):
+        wo, wl = _decimal_attention(q[0, h][None], k[0, h // g, :4], v[0, h // g, :4], 0.4, False)
+        np.testing.assert_allclose(o[0, h], wo[0], rtol=0, atol=1e-13)
+        assert abs(lse[0, h] - wl[0]) < 1e-13
 
 
 # --------------------------------------------------------------------------
