@@ -26,6 +26,7 @@ from .ref import (
     attention_ref,
     decode_ref,
     decode_gqa_ref,
+    attention_bwd_ref,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode
 
@@ -35,6 +36,7 @@ __all__ = [
     "attention_ref",
     "decode_ref",
     "decode_gqa_ref",
+    "attention_bwd_ref",
     "bf16_half_ulp",
     "o_excess",
     "check_prefill",

@@ -158,3 +158,34 @@ def decode_gqa_ref(q, k, v, scale, seqlens=None):
             o[b, h] = (e / l) @ v[b, kh, :n]
             lse[b, h] = m + np.log(l)
     return o, lse
+
+
+def attention_bwd_ref(q, k, v, do, scale, causal):
+    """Exact attention backward: the gradients of Σ dO ∘ O with respect to Q, K, V.
+
+    The chain rule through O = P V and the row softmax P = softmax(S),
+    S = scale · Q Kᵀ [+ causal mask] ([15-779 L5] §7.1):
+        dV = Pᵀ dO,   dP = dO Vᵀ,   dS = P ∘ (dP − D),   D_i = Σ_j P_ij dP_ij,
+        dQ = scale · dS K,   dK = scale · dSᵀ Q.
+    (The diag(p) − p pᵀ Jacobian of each softmax row gives dS.)  P is formed
+    with steps 1–3 of the standard algorithm, one (b, h) at a time.
+    q, k, v, do: [B, H, N, d].  Returns (dQ, dK, dV, D) as float64 arrays,
+    D of shape [B, H, N].
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    do = as_f64(do)
+    B, H, N, _ = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dd = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            p, _, _ = safe_softmax(scores(q[b, h], k[b, h], scale, causal))
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            dd[b, h] = (p * dp).sum(axis=1)
+            ds = p * (dp - dd[b, h][:, None])
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv, dd

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import scipy.special
 
-from oracle import attention_ref, decode_gqa_ref, decode_ref, safe_softmax, scores
+from oracle import attention_bwd_ref, attention_ref, decode_gqa_ref, decode_ref, safe_softmax, scores
 from oracle.compare import bf16_half_ulp, bf16_rne, check_prefill
 import _method_fp64 as M
 
@@ -380,6 +380,58 @@ def test_decode_gqa_matches_decimal_bruteforce():
         wo, wl = _decimal_attention(q[0, h][None], k[0, h // g, :4], v[0, h // g, :4], 0.4, False)
         np.testing.assert_allclose(o[0, h], wo[0], rtol=0, atol=1e-13)
         assert abs(lse[0, h] - wl[0]) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# backward
+
+
+def _loss(q, k, v, do, scale, causal):
+    return float((attention_ref(q, k, v, scale, causal)[0] * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    """dQ, dK, dV are the gradients of Σ dO ∘ O: central differences of the
+    forward definition (step 1e-5, fp64) agree to 1e-8 on a small problem."""
+    rng = np.random.default_rng(41 + causal)
+    B, H, N, d = 1, 2, 5, 3
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    scale = 0.7
+    dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal)
+    eps = 1e-5
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            up = _loss(q, k, v, do, scale, causal)
+            x[idx] = keep - eps
+            down = _loss(q, k, v, do, scale, causal)
+            x[idx] = keep
+            num[idx] = (up - down) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d_identity_and_shift_invariance(causal):
+    """D_i = Σ_j P_ij dP_ij equals dO_i · O_i ([15-779 L5] §7.3); every row of dS
+    sums to zero (softmax ignores a shift of its row), so Σ_j dK_j = 0."""
+    rng = np.random.default_rng(43 + causal)
+    q, k, v, do = (rng.standard_normal((2, 2, 37, 8)) for _ in range(4))
+    dq, dk, dv, dd = attention_bwd_ref(q, k, v, do, 0.35, causal)
+    o, _ = attention_ref(q, k, v, 0.35, causal)
+    np.testing.assert_allclose(dd, (do * o).sum(-1), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
+
+
+def test_backward_dv_with_constant_do_is_column_sums():
+    """dO = 1: dV_j = Σ_i P_ij (the column sums of P) in every column."""
+    rng = np.random.default_rng(45)
+    q, k, v = (rng.standard_normal((1, 1, 20, 4)) for _ in range(3))
+    _, _, dv, _ = attention_bwd_ref(q, k, v, np.ones((1, 1, 20, 4)), 0.5, True)
+    p, _, _ = safe_softmax(scores(q[0, 0], k[0, 0], 0.5, True))
+    np.testing.assert_allclose(dv[0, 0], np.repeat(p.sum(axis=0)[:, None], 4, axis=1), rtol=0, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
