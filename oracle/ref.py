@@ -160,7 +160,7 @@ def decode_gqa_ref(q, k, v, scale, seqlens=None):
     return o, lse
 
 
-def attention_bwd_ref(q, k, v, do, scale, causal):
+def attention_bwd_ref(q, k, v, do, scale, causal, o=None):
     """Exact attention backward: the gradients of Σ dO ∘ O with respect to Q, K, V.
 
     The chain rule through O = P V and the row softmax P = softmax(S),
@@ -169,6 +169,10 @@ def attention_bwd_ref(q, k, v, do, scale, causal):
         dQ = scale · dS K,   dK = scale · dSᵀ Q.
     (The diag(p) − p pᵀ Jacobian of each softmax row gives dS.)  P is formed
     with steps 1–3 of the standard algorithm, one (b, h) at a time.
+    With ``o`` given (a stored forward output [B, H, N, d]), D is taken as
+    D_i = Σ_c dO_ic O_ic, the identity of [15-779 L5] §7.3 that lets a
+    blockwise backward form D before its loops; it equals Σ_j P_ij dP_ij when
+    o is the exact O.
     q, k, v, do: [B, H, N, d].  Returns (dQ, dK, dV, D) as float64 arrays,
     D of shape [B, H, N].
     """
@@ -176,6 +180,7 @@ def attention_bwd_ref(q, k, v, do, scale, causal):
     k = as_f64(k)
     v = as_f64(v)
     do = as_f64(do)
+    o = None if o is None else as_f64(o)
     B, H, N, _ = q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     dd = np.empty((B, H, N), dtype=np.float64)
@@ -184,7 +189,7 @@ def attention_bwd_ref(q, k, v, do, scale, causal):
             p, _, _ = safe_softmax(scores(q[b, h], k[b, h], scale, causal))
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
-            dd[b, h] = (p * dp).sum(axis=1)
+            dd[b, h] = (p * dp).sum(axis=1) if o is None else (do[b, h] * o[b, h]).sum(axis=1)
             ds = p * (dp - dd[b, h][:, None])
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])

@@ -425,6 +425,31 @@ def test_backward_d_identity_and_shift_invariance(causal):
     np.testing.assert_allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_with_stored_output(causal):
+    """With the exact O passed in, D from dO · O gives the same gradients; an O
+    whose row i is off so that dO_i · O_i moves by c_i shifts dS_ij by −P_ij c_i,
+    hence dQ_i by −scale c_i (P K)_i and dK_j by −scale Σ_i c_i P_ij Q_i, and
+    leaves dV alone."""
+    rng = np.random.default_rng(47 + causal)
+    q, k, v, do = (rng.standard_normal((1, 2, 29, 8)) for _ in range(4))
+    scale = 0.4
+    o, _ = attention_ref(q, k, v, scale, causal)
+    base = attention_bwd_ref(q, k, v, do, scale, causal)
+    same = attention_bwd_ref(q, k, v, do, scale, causal, o=o)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    c = rng.standard_normal((1, 2, 29))
+    o_off = o + c[..., None] * do / (do * do).sum(-1, keepdims=True)
+    dq, dk, dv, dd = attention_bwd_ref(q, k, v, do, scale, causal, o=o_off)
+    np.testing.assert_allclose(dd, base[3] + c, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, base[2], rtol=0, atol=1e-13)
+    for h in range(2):
+        p, _, _ = safe_softmax(scores(q[0, h], k[0, h], scale, causal))
+        np.testing.assert_allclose(dq[0, h] - base[0][0, h], -scale * c[0, h][:, None] * (p @ k[0, h]), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk[0, h] - base[1][0, h], -scale * (p * c[0, h][:, None]).T @ q[0, h], rtol=0, atol=1e-12)
+
+
 def test_backward_dv_with_constant_do_is_column_sums():
     """dO = 1: dV_j = Σ_i P_ij (the column sums of P) in every column."""
     rng = np.random.default_rng(45)
