@@ -28,7 +28,7 @@ from .ref import (
     decode_gqa_ref,
     attention_bwd_ref,
 )
-from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode
+from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode, bwd_allowance, check_bwd
 
 __all__ = [
     "scores",
@@ -41,4 +41,6 @@ __all__ = [
     "o_excess",
     "check_prefill",
     "check_decode",
+    "bwd_allowance",
+    "check_bwd",
 ]

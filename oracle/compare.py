@@ -14,6 +14,10 @@ correct rounding:
 The report also carries the literal max-abs error, the rounding floor
 max|bf16_RNE(O_ref) − O_ref| and the excess max(|err| − ½ulp) so that the
 literal reading can be judged too.
+
+The backward has no stated tolerance; ``bwd_allowance`` derives one per
+element from the arithmetic of a backward that feeds P and dS to the matrix
+products as bf16 and accumulates in fp32 (see its docstring).
 """
 
 import numpy as np
@@ -68,3 +72,72 @@ def check_prefill(o_gpu, lse_gpu, o_ref, lse_ref):
 
 
 check_decode = check_prefill
+
+U_BF16 = 2.0 ** -8   # unit roundoff of round-to-nearest bf16 (8 significant bits)
+U_F32 = 2.0 ** -24
+
+
+def bwd_allowance(q, k, v, do, scale, causal, o=None, p_rel=0.0, o_err=None):
+    """Per-element error allowance of a bf16-operand, fp32-accumulating backward.
+
+    Reference values are those of ``attention_bwd_ref`` (same arguments).  The
+    kernel under test forms P = exp(scale·q·k − L) in fp32, D_i = Σ dO_i O_i
+    and dP = dO Vᵀ as fp32 sums of exact bf16 products, dS = P (dP − D), and
+    rounds P and dS to bf16 before the products dV = Pᵀ dO, dK = scale·dSᵀ Q,
+    dQ = scale·dS K, which accumulate in fp32.  Per element:
+
+        |ΔP| ≤ u_P·P,  u_P = 2^-8 (bf16) + 2^-16 (fp32 exponent and exp2) + p_rel
+        |ΔdS| ≤ u_P·|dS| + P·(γ_d·(|dO||V|ᵀ + Σ_c|dO_c O_c|) + Σ_c |dO_c|·o_err_c)
+        |ΔdV| ≤ (u_P + γ_N)·Pᵀ|dO|
+        |ΔdK| ≤ scale·(|ΔdS|ᵀ|Q| + γ_N·|dS|ᵀ|Q|),   |ΔdQ| likewise with |K|
+    with γ_n = n·2^-24 (fp32 sums of n terms).  ``p_rel`` covers an L that is
+    itself a computed value; ``o_err`` [B, H, N, d] bounds |O_given − O| where
+    the kernel's O differs from the one the reference uses for D.
+    Returns ((dq, dk, dv) reference, (dq, dk, dv) allowance), all float64;
+    the output rounding to bf16 is added by ``check_bwd``.
+    """
+    from .ref import as_f64, attention_ref, safe_softmax, scores, attention_bwd_ref
+
+    dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal, o=o)
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    if o is None:
+        o, _ = attention_ref(q, k, v, scale, causal)
+    o = as_f64(o)
+    B, H, N, d = q.shape
+    u_p = U_BF16 + 2.0 ** -16 + p_rel
+    g_d, g_n = d * U_F32, N * U_F32
+    aq, ak, av = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            p, _, _ = safe_softmax(scores(q[b, h], k[b, h], scale, causal))
+            ado = np.abs(do[b, h])
+            dp = do[b, h] @ v[b, h].T
+            dd = (do[b, h] * o[b, h]).sum(axis=1)
+            ds = np.abs(p * (dp - dd[:, None]))
+            dmag = (ado * np.abs(o[b, h])).sum(axis=1)
+            if o_err is not None:
+                dmag = dmag + (ado * np.asarray(o_err[b, h], dtype=np.float64)).sum(axis=1) / g_d
+            e_ds = u_p * ds + p * g_d * (ado @ np.abs(v[b, h]).T + dmag[:, None])
+            av[b, h] = (u_p + g_n) * (p.T @ ado)
+            ak[b, h] = scale * ((e_ds + g_n * ds).T @ np.abs(q[b, h]))
+            aq[b, h] = scale * ((e_ds + g_n * ds) @ np.abs(k[b, h]))
+    return (dq, dk, dv), (aq, ak, av)
+
+
+def check_bwd(got, ref, allow):
+    """|x − x_ref| ≤ allowance + ½ulp_bf16(|x_ref| + allowance) for x in (dQ, dK, dV).
+
+    ``got``, ``ref``, ``allow``: triples of arrays.  Returns a report with the
+    literal max-abs error, the largest error/limit ratio per gradient and
+    ``pass``."""
+    rep = {"pass": True}
+    for name, g, r, a in zip(("dq", "dk", "dv"), got, ref, allow):
+        g = np.asarray(g, dtype=np.float64)
+        err = np.abs(g - r)
+        lim = a + bf16_half_ulp(np.abs(r) + a)
+        rep[name + "_max_abs"] = float(err.max()) if err.size else 0.0
+        rep[name + "_ratio"] = float((err / lim).max()) if err.size else 0.0
+        ok = bool(np.all(err <= lim)) and bool(np.all(np.isfinite(g)))
+        rep[name + "_ok"] = ok
+        rep["pass"] = rep["pass"] and ok
+    return rep

@@ -6,7 +6,8 @@ here, so the two sides see the same bytes.
 
 Recipe (every tensor is bf16, i.i.d. N(0, 1)):
 
-* Prefill q, k, v and decode q: one torch ``Generator`` per (workload, tensor, b, h), seeded with
+* Prefill q, k, v, the backward's output gradient dO, and decode q: one
+  torch ``Generator`` per (workload, tensor, b, h), seeded with
   ``seed_for(...)``, so any single head can be regenerated on its own.
 * ``torch.randn`` in float32, then round-to-nearest-even to bfloat16.
 * The Llama-3-8B-shaped workload scales 1 % of the key rows of every (b, h) by
@@ -76,7 +77,7 @@ EXTRA_WORKLOADS = [
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
-_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3, "seqlens": 4}
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3, "seqlens": 4, "do": 5}
 
 
 def seed_for(w: Workload, tensor: str, b: int, h: int) -> int:
@@ -121,6 +122,22 @@ def make_prefill(w: Workload):
                 x[b, h] = prefill_head(w, t, b, h)
         out.append(x)
     return tuple(out)
+
+
+def make_prefill_grad(w: Workload) -> torch.Tensor:
+    """The output gradient dO [B, H, N, d] (CPU, bf16, i.i.d. N(0, 1)) for the backward."""
+    x = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16)
+    for b in range(w.B):
+        for h in range(w.H):
+            x[b, h] = randn_bf16(seed_for(w, "do", b, h), (w.N, w.d))
+    return x
+
+
+def bwd_flops(w: Workload) -> float:
+    """The backward's algorithmic FLOPs: five N×N×d products (S, dP, dV, dK, dQ),
+    10·N²·d·B·H, halved when causal — 2.5 times the forward's."""
+    f = 10.0 * w.N * w.N * w.d * w.B * w.H
+    return f / 2 if w.causal else f
 
 
 def make_decode_q(w: Workload) -> torch.Tensor:

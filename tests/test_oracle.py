@@ -18,7 +18,7 @@ import pytest
 import scipy.special
 
 from oracle import attention_bwd_ref, attention_ref, decode_gqa_ref, decode_ref, safe_softmax, scores
-from oracle.compare import bf16_half_ulp, bf16_rne, check_prefill
+from oracle.compare import bf16_half_ulp, bf16_rne, bwd_allowance, check_bwd, check_prefill
 import _method_fp64 as M
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "closed_form_4tok.json")
@@ -475,6 +475,66 @@ def test_bf16_rounding_helpers():
     assert r["pass"] and r["floor"] > 0
     r = check_prefill(x + 0.02, [0.0], x, [0.0])
     assert not r["ok"]
+
+
+# --------------------------------------------------------------------------
+# the backward allowance: wide enough for a faithful bf16-operand backward,
+# narrow enough to fail plausible slips
+
+
+def _sim_bwd(q, k, v, do, o, lse, scale, causal, slip=None):
+    """A bf16-operand, fp32-accumulating backward in numpy float32 (the arithmetic
+    bwd_allowance describes), with an optional planted slip."""
+    f = np.float32
+    c = f(scale * math.log2(math.e))
+    out = [np.empty(q.shape, np.float64) for _ in range(3)]
+    N = q.shape[2]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            qq, kk, vv, dd_o, oo = (np.asarray(x[b, h], dtype=f) for x in (q, k, v, do, o))
+            l2 = np.asarray(lse[b, h], dtype=f) * f(math.log2(math.e))
+            s = qq @ kk.T
+            p = np.exp2(s * c - (l2[:, None] if slip != "no_lse" else f(0)))
+            if causal and slip != "no_mask":
+                p[np.triu_indices(N, 1)] = 0
+            dp = dd_o @ vv.T
+            dvec = (dd_o * oo).sum(axis=1)
+            ds = p * (dp - (dvec[:, None] if slip != "no_d" else f(0)))
+            pb = bf16_rne(p).astype(f)
+            sb = bf16_rne(ds).astype(f)
+            sc = f(1.0) if slip == "no_scale" else f(scale)
+            out[2][b, h] = bf16_rne((pb if slip == "dv_untransposed" else pb.T) @ dd_o)
+            out[1][b, h] = bf16_rne(sc * (sb.T @ qq))
+            out[0][b, h] = bf16_rne(sc * (sb @ kk))
+    return out
+
+
+def _bwd_case(causal, seed, N=48, d=16):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (bf16_rne(rng.standard_normal((1, 2, N, d))) for _ in range(4))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = attention_ref(q, k, v, scale, causal)
+    return q, k, v, do, bf16_rne(o), np.asarray(lse, dtype=np.float32), scale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_allowance_admits_a_faithful_bf16_backward(causal):
+    q, k, v, do, o, lse, scale = _bwd_case(causal, 51 + causal)
+    ref, allow = bwd_allowance(q, k, v, do, scale, causal, o=o)
+    rep = check_bwd(_sim_bwd(q, k, v, do, o, lse, scale, causal), ref, allow)
+    assert rep["pass"], rep
+    # and it is not vacuous: the limits are a small fraction of the gradients' size
+    for r, a in zip(ref, allow):
+        assert np.median(a) < 0.05 * np.median(np.abs(r))
+
+
+@pytest.mark.parametrize("slip", ["no_d", "no_mask", "no_scale", "no_lse", "dv_untransposed"])
+def test_bwd_allowance_rejects_slips(slip):
+    causal = True
+    q, k, v, do, o, lse, scale = _bwd_case(causal, 53)
+    ref, allow = bwd_allowance(q, k, v, do, scale, causal, o=o)
+    rep = check_bwd(_sim_bwd(q, k, v, do, o, lse, scale, causal, slip=slip), ref, allow)
+    assert not rep["pass"], (slip, rep)
 
 
 # --------------------------------------------------------------------------
