@@ -77,7 +77,7 @@ U_BF16 = 2.0 ** -8   # unit roundoff of round-to-nearest bf16 (8 significant bit
 U_F32 = 2.0 ** -24
 
 
-def bwd_allowance(q, k, v, do, scale, causal, o=None, p_rel=0.0, o_err=None):
+def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False):
     """Per-element error allowance of a bf16-operand, fp32-accumulating backward.
 
     Reference values are those of ``attention_bwd_ref`` (same arguments).  The
@@ -86,13 +86,17 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, p_rel=0.0, o_err=None):
     rounds P and dS to bf16 before the products dV = Pᵀ dO, dK = scale·dSᵀ Q,
     dQ = scale·dS K, which accumulate in fp32.  Per element:
 
-        |ΔP| ≤ u_P·P,  u_P = 2^-8 (bf16) + 2^-16 (fp32 exponent and exp2) + p_rel
-        |ΔdS| ≤ u_P·|dS| + P·(γ_d·(|dO||V|ᵀ + Σ_c|dO_c O_c|) + Σ_c |dO_c|·o_err_c)
+        |ΔP| ≤ u_P·P,  u_P = 2^-8 (bf16) + 2^-16 (fp32 exponent and exp2)
+        |ΔdS| ≤ u_P·|dS| + P·γ_d·(|dO||V|ᵀ + Σ_c|dO_c O_c|)
         |ΔdV| ≤ (u_P + γ_N)·Pᵀ|dO|
         |ΔdK| ≤ scale·(|ΔdS|ᵀ|Q| + γ_N·|dS|ᵀ|Q|),   |ΔdQ| likewise with |K|
-    with γ_n = n·2^-24 (fp32 sums of n terms).  ``p_rel`` covers an L that is
-    itself a computed value; ``o_err`` [B, H, N, d] bounds |O_given − O| where
-    the kernel's O differs from the one the reference uses for D.
+    with γ_n = n·2^-24 (fp32 sums of n terms).
+    ``o_from_fwd``: the kernel's O and L come from a forward of the same
+    arithmetic (weights P̃ rounded to bf16 in both the sum Σ P̃ v and its
+    normaliser, fp32 sums) while the reference uses the exact O; then
+        |O_kernel − O| ≤ o_err = ulp_bf16(O) + (2·2^-8 + γ_N)·P|V|,
+    which enters |ΔdS| as P·Σ_c |dO_c|·o_err_c, and the fp32 sum inside L
+    adds p_rel = γ_N + 2^-20 to u_P.
     Returns ((dq, dk, dv) reference, (dq, dk, dv) allowance), all float64;
     the output rounding to bf16 is added by ``check_bwd``.
     """
@@ -104,8 +108,8 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, p_rel=0.0, o_err=None):
         o, _ = attention_ref(q, k, v, scale, causal)
     o = as_f64(o)
     B, H, N, d = q.shape
-    u_p = U_BF16 + 2.0 ** -16 + p_rel
     g_d, g_n = d * U_F32, N * U_F32
+    u_p = U_BF16 + 2.0 ** -16 + ((g_n + 2.0 ** -20) if o_from_fwd else 0.0)
     aq, ak, av = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
         for h in range(H):
@@ -115,8 +119,9 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, p_rel=0.0, o_err=None):
             dd = (do[b, h] * o[b, h]).sum(axis=1)
             ds = np.abs(p * (dp - dd[:, None]))
             dmag = (ado * np.abs(o[b, h])).sum(axis=1)
-            if o_err is not None:
-                dmag = dmag + (ado * np.asarray(o_err[b, h], dtype=np.float64)).sum(axis=1) / g_d
+            if o_from_fwd:
+                o_err = bf16_ulp(o[b, h]) + (2 * U_BF16 + g_n) * (p @ np.abs(v[b, h]))
+                dmag = dmag + (ado * o_err).sum(axis=1) / g_d
             e_ds = u_p * ds + p * g_d * (ado @ np.abs(v[b, h]).T + dmag[:, None])
             av[b, h] = (u_p + g_n) * (p.T @ ado)
             ak[b, h] = scale * ((e_ds + g_n * ds).T @ np.abs(q[b, h]))

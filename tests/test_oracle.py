@@ -528,6 +528,28 @@ def test_bwd_allowance_admits_a_faithful_bf16_backward(causal):
         assert np.median(a) < 0.05 * np.median(np.abs(r))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_allowance_covers_forward_then_backward(causal):
+    """O and L from a float32 forward that rounds its weights to bf16, fed to the
+    simulated backward, against the exact reference: within the o_from_fwd limits."""
+    q, k, v, do, _, _, scale = _bwd_case(causal, 55 + causal, N=64, d=32)
+    f = np.float32
+    o = np.empty(q.shape)
+    lse = np.empty(q.shape[:3], dtype=f)
+    for h in range(q.shape[1]):
+        s = np.asarray(q[0, h], dtype=f) @ np.asarray(k[0, h], dtype=f).T * f(scale)
+        if causal:
+            s[np.triu_indices(q.shape[2], 1)] = -np.inf
+        m = s.max(axis=1, keepdims=True)
+        pt = np.exp(s - m)
+        pb = bf16_rne(pt).astype(f)
+        o[0, h] = bf16_rne((pb @ np.asarray(v[0, h], dtype=f)) / pb.sum(axis=1, keepdims=True))
+        lse[0, h] = m[:, 0] + np.log(pt.sum(axis=1))
+    ref, allow = bwd_allowance(q, k, v, do, scale, causal, o_from_fwd=True)
+    rep = check_bwd(_sim_bwd(q, k, v, do, o, lse, scale, causal), ref, allow)
+    assert rep["pass"], rep
+
+
 @pytest.mark.parametrize("slip", ["no_d", "no_mask", "no_scale", "no_lse", "dv_untransposed"])
 def test_bwd_allowance_rejects_slips(slip):
     causal = True
