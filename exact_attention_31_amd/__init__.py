@@ -10,6 +10,8 @@ library is missing or fails to load, the calls raise.
     fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
     fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None) -> (o, lse)
     fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
+    fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+    fa_bwd_workspace_bytes(B, H, N)                  -> int
     fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
     fa_fwd_tile_shape(d)                             -> (block_m, block_n)
     fa_status_str(status)                            -> str
@@ -54,6 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode.restype = i
     lib.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, vp, sz, vp]
     lib.fa_decode_gqa.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_fwd_tile_pairs.argtypes = [i, i, i]
@@ -90,6 +96,10 @@ def fa_fwd_tile_shape(d: int):
 
 def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(load_library().fa_decode_workspace_bytes(int(B), int(H), int(d), int(num_splits)))
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
 
 
 def _torch():
@@ -230,3 +240,37 @@ def fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None, workspace=
     if st != FA_OK:
         raise FaError(st, "fa_decode_gqa")
     return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
+    """Backward of fa_fwd: q, k, v, o, do bf16 [B, H, N, d], lse fp32 [B, H, N]
+    (o and lse as fa_fwd returned them, do the gradient with respect to o).
+
+    Returns (dq, dk, dv), bf16 [B, H, N, d].  ``scale`` and ``causal`` must be
+    the forward's.  The workspace (fa_bwd_workspace_bytes) is allocated with
+    torch when not given.  Runs on the current stream.
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, 4)
+    if not (q.shape == k.shape == v.shape == o.shape == do.shape):
+        raise ValueError("q, k, v, o, do must have one shape")
+    if len({t.device for t in (q, k, v, o, do, lse)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    B, H, N, d = q.shape
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or lse.shape != (B, H, N) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                               float(scale), int(bool(causal)), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

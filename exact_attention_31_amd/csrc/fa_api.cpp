@@ -42,7 +42,7 @@ const char* fa_status_str(int s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
     case FA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case FA_ERR_VALUE: return "scale not positive and finite, or num_splits outside [1, Lkv]";
-    case FA_ERR_WORKSPACE: return "decode workspace missing or smaller than required";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIAS: return "an output overlaps an input";
     default: return "unknown status";
@@ -97,6 +97,65 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   if (fa::launch_fwd(p, d, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  const unsigned long long rows = (unsigned long long)B * H * N;
+  if (rows > 0x7fffffffull) return 0;
+  return (size_t)rows * 8;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t elems = count4(B, H, N, d);
+  if (elems == 0 || (unsigned long long)N * d * 2 > 0x7fff0000ull || (unsigned long long)B * H * N > 0x7fffffffull ||
+      (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_bytes[4] = {tb, tb, tb, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.ld = static_cast<float*>(workspace);
+  p.BH = B * H;
+  p.N = N;
+  p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
+  p.n_kblk = fa::ceil_div(N, fa::kBwdBlockK);
+  const long long tq = (long long)p.BH * p.n_qblk, tk = (long long)p.BH * p.n_kblk;
+  p.xcd_remap_q = (tq % 8 == 0) && ((tq / 8) % p.n_qblk == 0);
+  p.xcd_remap_k = (tk % 8 == 0) && ((tk / 8) % p.n_kblk == 0);
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  if (fa::launch_bwd(p, d, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }
 

@@ -1,0 +1,529 @@
+// Exact-attention backward for CDNA4 (gfx950): dQ, dK, dV from Q, K, V, the
+// forward output O, its log-sum-exp L and the output gradient dO.
+//
+// The N×N probabilities are never stored: every kernel recomputes the tile
+// it needs as P = exp(scale·Q Kᵀ − L) from the saved L, which already holds
+// each row's normalisation, so no online softmax is needed here
+// ([15-779 L5] §7.2; [cicada] §3.2.3 keeps L for exactly this).  With
+// D_i = dO_i · O_i formed once per row before the loops ([15-779 L5] §7.3),
+// each tile's gradient of the scores is local:
+//     dP = dO Vᵀ,   dS = P ∘ (dP − D),
+//     dV = Σ Pᵀ dO,   dK = scale · Σ dSᵀ Q,   dQ = scale · Σ dS K.
+// ([15-779 L5] §7.1; [pinghaoyang FA-1] "Backward".)
+//
+// Three kernels, in stream order:
+//   fa_bwd_prep   per row: (L·log2 e, D) into the workspace;
+//   fa_bwd_dkdv   key/value blocks outside, query tiles inside — the loop
+//                 order of [15-779 L5] §7.4: a workgroup keeps dK and dV of
+//                 its 128 keys in registers and writes them once;
+//   fa_bwd_dq     query blocks outside, key/value tiles inside, as in the
+//                 forward: dQ of 256 query rows stays in registers.
+// dQ is not accumulated with atomic adds from the key-block kernel (the
+// scheme of [15-779 L5] §7.4); its own pass recomputes S and dP instead,
+// which costs two more tile products (seven in all, against five) but keeps
+// the result deterministic and needs no fp32 dQ buffer or atomic traffic.
+//
+// Layout on chip (64-lane wavefronts, v_mfma_f32_32x32x16_bf16):
+// * dkdv: each wavefront owns 32 keys.  The products are taken so that a
+//   lane's accumulator column is one key: S = Q Kᵀ and dP = dO Vᵀ with the
+//   key rows of K and V held in registers as the B operands; P and dS then
+//   sit in the layout of the B operand of dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS,
+//   whose A operands are read from the Q and dO tiles in LDS with the
+//   transpose load ds_read_b64_tr_b16.
+// * dq: each wavefront owns 32 query rows, lane = query column as in the
+//   forward: Sᵀ = K Qᵀ and dPᵀ = V dOᵀ with Q and dO rows in registers, so
+//   L and D are one scalar per lane; dSᵀ feeds dQᵀ += Kᵀ dSᵀ directly, Kᵀ
+//   again read with the transpose load.
+// * Tiles in LDS are row-major with the 16-byte chunk index XOR-ed with a
+//   function of the row that keeps both the 16-byte row reads (16 rows, one
+//   chunk) and the transpose reads (4 rows, 64 bytes each) on distinct banks.
+//   Tiles are filled by buffer loads that write LDS directly, two stages
+//   ahead of use; rows past N read as zero.
+//
+// Pages cited: [15-779 L5] "第 5 讲 · 案例：Transformer、注意力与 FlashAttention";
+// [cicada] "已有的几种大模型上下文支持情况"; [pinghaoyang FA-1] "FlashAttention
+// 完全拆解（一）".
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdStages = 3;  // LDS stages per tensor (loops are unrolled by this)
+
+template <int D>
+struct BwdTile {
+  static constexpr int CH = D / 8;        // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;       // bytes per row in LDS (unpadded)
+  static constexpr int RPR = 1024 / ROW;  // rows filled by one wavefront-wide 16-byte direct load
+  static constexpr int KS = D / 16;       // MFMA k-steps over d
+  static constexpr int DSUB = D / 32;     // 32-wide sub-tiles over d
+  // Chunk swizzle, period 16 rows.  D = 128 (16 chunks a row): 16 consecutive
+  // rows take 16 distinct values (row reads), and the 4 rows of an aligned
+  // group differ in bits 2-3 (transpose reads touch 4 chunks of each of 4
+  // rows).  D = 64 (8 chunks): the same for rows of equal parity, whose bank
+  // halves coincide.
+  __device__ static int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+};
+
+// Buffer loads into registers; bytes at or past num_records read as zero.
+__device__ inline u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+__device__ inline float2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+
+// Lane offsets into a tile of BwdTile<D> rows.
+template <int D>
+struct TileReads {
+  using T = BwdTile<D>;
+  int row[T::KS];    // 16-byte row reads: row i32 (+32 per sub-tile), chunk 2kk + g
+  int tr0[T::DSUB];  // transpose reads, rows 4g + jj/4 (+16 per k-step)
+  int tr8[T::DSUB];  // the same 8 rows further on (the swizzle has period 16)
+  __device__ void init(int lane) {
+    const int i32 = lane & 31, g = lane >> 5, jj = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) row[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::swz(i32)) << 4);
+    const int r = 4 * g + (jj >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds) {
+      tr0[ds] = r * T::ROW + (((4 * ds + cl) ^ T::swz(r)) << 4) + 8 * (jj & 1);
+      tr8[ds] = (r + 8) * T::ROW + (((4 * ds + cl) ^ T::swz(r + 8)) << 4) + 8 * (jj & 1);
+    }
+  }
+  // A operand of one k-step (16 rows) of a product whose reduction index is the row.
+  __device__ bf16x8_t tr(const unsigned char* b, int ds, int kk) const {
+    const u32x2_t a0 = lds_tr_read(b, tr0[ds] + 16 * kk * T::ROW);
+    const u32x2_t a1 = lds_tr_read(b, tr8[ds] + 16 * kk * T::ROW);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+  }
+  // A operand of one k-step (16 of d) for the 32 rows of sub-tile `sub`.
+  __device__ bf16x8_t rows(const unsigned char* b, int kk, int sub) const {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(b + row[kk] + sub * 32 * T::ROW));
+  }
+};
+
+// Direct loads of a tile: wavefront-wide load x fills LDS bytes [1024x, +1024),
+// i.e. rows x·RPR .. +RPR-1 with their chunks swizzled.  `goff` is the global
+// offset of the lane's chunk for run x0; runs x0 + 16/RPR·i share it up to a
+// shift of the tile offset (the swizzle repeats every 16 rows).
+template <int D>
+__device__ inline int run_goff(int x0, int lane) {
+  using T = BwdTile<D>;
+  const int r = x0 * T::RPR + lane / T::CH;
+  return r * T::ROW + (((lane % T::CH) ^ T::swz(r)) << 4);
+}
+
+// Packs 8 fp32 accumulator elements r0 .. r0+7 as the bf16 B operand of a
+// product reducing over the accumulator's rows (row order as in the forward).
+__device__ inline bf16x8_t pack8(const float* x) {
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// ---- per-row statistics: (L·log2 e, D = dO·O) ---------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
+  constexpr int CH = D / 8;
+  const int rows_total = p.BH * p.N;
+  const int row = blockIdx.x * (256 / CH) + threadIdx.x / CH;
+  const int c = threadIdx.x % CH;
+  float acc = 0.f;
+  if (row < rows_total) {
+    const u32x4_t o = reinterpret_cast<const u32x4_t*>(p.o + (size_t)row * D)[c];
+    const u32x4_t g = reinterpret_cast<const u32x4_t*>(p.dout + (size_t)row * D)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(g[e] << 16), acc);
+      acc = fmaf(__uint_as_float(o[e] & 0xffff0000u), __uint_as_float(g[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int w = CH / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, CH);
+  if (row < rows_total && c == 0)
+    reinterpret_cast<float2*>(p.ld)[row] = make_float2(p.lse[row] * 1.4426950408889634f, acc);
+}
+
+// ---- dK, dV: key blocks outside, query tiles inside ------------------------------
+__device__ inline void decode_kblock(const BwdParams& p, int& bh, int& kb) {
+  const int x = blockIdx.x;
+  if (p.xcd_remap_k) {  // whole heads per XCD; within an XCD the heaviest blocks (first keys) first
+    const int per_xcd = (p.BH * p.n_kblk) >> 3;
+    const int heads_per_xcd = per_xcd / p.n_kblk;
+    const int local = x >> 3;
+    bh = (x & 7) * heads_per_xcd + local % heads_per_xcd;
+    kb = local / heads_per_xcd;
+  } else {
+    bh = x % p.BH;
+    kb = x / p.BH;
+  }
+}
+
+// One wavefront per SIMD: the dK and dV accumulators (32 keys × d each),
+// the K and V rows and two 32-row score tiles need more than the 256
+// registers a lane has when two wavefronts share a SIMD.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int W = kBwdKvWaves;
+  constexpr int BM = 64;              // query rows per step (two 32-row sub-tiles)
+  constexpr int QT = BM * T::ROW;     // bytes of one Q (or dO) stage
+  constexpr int R = BM / T::RPR;      // direct loads per tensor per stage
+  static_assert(2 * R % W == 0 && (W * T::RPR) % 16 == 0, "stage loads spread evenly, one lane offset");
+  constexpr int PER = 2 * R / W;      // tile loads per wavefront per stage
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds0[QT], q_lds1[QT], q_lds2[QT];
+  __shared__ __attribute__((aligned(16))) unsigned char o_lds0[QT], o_lds1[QT], o_lds2[QT];
+  __shared__ __attribute__((aligned(16))) float l_lds0[2 * BM], l_lds1[2 * BM], l_lds2[2 * BM];
+  unsigned char* const qbufs[3] = {q_lds0, q_lds1, q_lds2};
+  unsigned char* const obufs[3] = {o_lds0, o_lds1, o_lds2};
+  float* const lbufs[3] = {l_lds0, l_lds1, l_lds2};
+
+  int bh, kb;
+  decode_kblock(p, bh, kb);
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i32 = lane & 31, g = lane >> 5;
+  const int k0 = kb * kBwdBlockK;
+  const int kw = k0 + 32 * wave_u;  // first key of this wavefront
+  const int key = kw + i32;         // the key of this lane's accumulator column
+  const size_t base = (size_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc(p.q + base, N * T::ROW);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(p.dout + base, N * T::ROW);
+  const __amdgpu_buffer_rsrc_t lrsrc = make_rsrc(p.ld + (size_t)bh * N * 2, N * 8);
+
+  // K and V rows of this lane's key: the B operands of S = Q Kᵀ and dP = dO Vᵀ.
+  bf16x8_t kf[T::KS], vf[T::KS];
+  {
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) {
+      kf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(krsrc, key * T::ROW + (2 * kk + g) * 16));
+      vf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(vrsrc, key * T::ROW + (2 * kk + g) * 16));
+    }
+  }
+
+  TileReads<D> rd;
+  rd.init(lane);
+
+  const int first = CAUSAL ? k0 / BM : 0;  // query tiles before the block's first key see none of it
+  const int n_steps = ceil_div(N, BM) - first;
+  // Stage loads: wavefront w issues loads w, w + W, ... of the 2R runs (Q
+  // runs first, then dO); the lane's offset is the same for all of them.
+  const int x0 = wave_u % R;
+  const int goff = run_goff<D>(x0, lane);
+  auto issue = [&](int s, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int toff = (first + s) * QT;  // byte offset of the stage's first row
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = wave_u + i * W;  // uniform
+      if (x < R)
+        load_lds16(qrsrc, qbufs[B] + x * 1024, goff + toff + (x - x0) * 1024);
+      else
+        load_lds16(orsrc, obufs[B] + (x - R) * 1024, goff + toff + (x - R - x0) * 1024);
+    }
+    if (wave_u == 0) load_lds4(lrsrc, lbufs[B], lane * 4 + (first + s) * BM * 8);
+    if (wave_u == 1) load_lds4(lrsrc, lbufs[B] + 64, lane * 4 + (first + s) * BM * 8 + 256);
+  };
+  auto wait_stage = [&](bool more) {  // own loads of the oldest stage in flight have landed
+    if (!more)
+      wait_vmcnt<0>();
+    else if (wave_u <= 1)
+      wait_vmcnt<PER + 1>();
+    else
+      wait_vmcnt<PER>();
+  };
+
+  f32x16_t dk[T::DSUB], dv[T::DSUB];
+#pragma unroll
+  for (int ds = 0; ds < T::DSUB; ++ds) dk[ds] = dv[ds] = f32x16_t{};
+  const float c = p.scale_log2;
+
+  auto step = [&](int s, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int qs0 = (first + s) * BM;
+    if (CAUSAL && qs0 + BM - 1 < kw) return;  // every query of the tile precedes this wavefront's keys
+    const unsigned char* qb = qbufs[B];
+    const unsigned char* ob = obufs[B];
+    f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sacc[u] = dpacc[u] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(qb, kk, u), kf[kk], sacc[u], 0, 0, 0);
+        dpacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(ob, kk, u), vf[kk], dpacc[u], 0, 0, 0);
+      }
+    const bool diag = CAUSAL && qs0 < kw + 32;  // some query of the tile precedes some key
+    const float* lb = lbufs[B];
+    float pr[32], dsr[32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // (L·log2 e, D) of accumulator rows 32u + 8t + 4g + (0..3)
+        const float4 a = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g));
+        const float4 b = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g + 2));
+        const float l2[4] = {a.x, a.z, b.x, b.z}, dd[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * t + i;
+          float e = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], c, -l2[i]));
+          if (diag && key > qs0 + 32 * u + 8 * t + 4 * g + i) e = 0.f;
+          pr[16 * u + r] = e;
+          dsr[16 * u + r] = e * (dpacc[u][r] - dd[i]);
+        }
+      }
+#pragma unroll
+    for (int kk = 0; kk < BM / 16; ++kk) {
+      const bf16x8_t pb = pack8(pr + 8 * kk), sb = pack8(dsr + 8 * kk);
+#pragma unroll
+      for (int ds = 0; ds < T::DSUB; ++ds) {
+        dv[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(ob, ds, kk), pb, dv[ds], 0, 0, 0);
+        dk[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(qb, ds, kk), sb, dk[ds], 0, 0, 0);
+      }
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue(0, I0{});
+  if (n_steps > 1) issue(1, I1{});
+  wait_stage(n_steps > 1);
+  // K and V were loaded before the stages, so they are in: settle the
+  // compiler's load tracking for them once, outside the loop.
+#pragma unroll
+  for (int kk = 0; kk < T::KS; ++kk)
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, kf[kk])), "v"(__builtin_bit_cast(u32x4_t, vf[kk])));
+  auto body = [&](int s, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    wait_stage(s + 1 < n_steps);
+    block_barrier();  // stage s is in LDS for everyone; stage s-1's buffers are free
+    if (s + 2 < n_steps) issue(s + 2, std::integral_constant<int, (B + 2) % 3>{});
+    step(s, buf);
+  };
+  for (int s = 0; s < n_steps; s += 3) {
+    body(s, I0{});
+    if (s + 1 < n_steps) body(s + 1, I1{});
+    if (s + 2 < n_steps) body(s + 2, I2{});
+  }
+
+  // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, one store each ------------------
+  if (key < N) {
+    uint16_t* krow = p.dk + base + (size_t)key * D;
+    uint16_t* vrow = p.dv + base + (size_t)key * D;
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = ds * 32 + r4 * 8 + g * 4;
+        u32x2_t w;
+        w[0] = pack_bf16x2(dk[ds][4 * r4 + 0] * p.scale, dk[ds][4 * r4 + 1] * p.scale);
+        w[1] = pack_bf16x2(dk[ds][4 * r4 + 2] * p.scale, dk[ds][4 * r4 + 3] * p.scale);
+        *reinterpret_cast<u32x2_t*>(krow + d0) = w;
+        w[0] = pack_bf16x2(dv[ds][4 * r4 + 0], dv[ds][4 * r4 + 1]);
+        w[1] = pack_bf16x2(dv[ds][4 * r4 + 2], dv[ds][4 * r4 + 3]);
+        *reinterpret_cast<u32x2_t*>(vrow + d0) = w;
+      }
+  }
+}
+
+// ---- dQ: query blocks outside, key/value tiles inside -----------------------------
+__device__ inline void decode_qblock(const BwdParams& p, int& bh, int& qb) {
+  const int x = blockIdx.x;
+  if (p.xcd_remap_q) {  // whole heads per XCD; the heaviest blocks (last rows, when causal) first
+    const int per_xcd = (p.BH * p.n_qblk) >> 3;
+    const int heads_per_xcd = per_xcd / p.n_qblk;
+    const int local = x >> 3;
+    bh = (x & 7) * heads_per_xcd + local % heads_per_xcd;
+    qb = p.n_qblk - 1 - local / heads_per_xcd;
+  } else {
+    bh = x % p.BH;
+    qb = p.n_qblk - 1 - x / p.BH;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int BN = 64;              // keys per tile
+  constexpr int KT = BN * T::ROW;     // bytes of one K (or V) stage
+  constexpr int R = BN / T::RPR;      // direct loads per tensor per stage
+  static_assert(2 * R % kFwdWaves == 0 && (kFwdWaves * T::RPR) % 16 == 0, "stage loads share one lane offset");
+  constexpr int PER = 2 * R / kFwdWaves;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[KT], k_lds1[KT], k_lds2[KT];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[KT], v_lds1[KT], v_lds2[KT];
+  unsigned char* const kbufs[3] = {k_lds0, k_lds1, k_lds2};
+  unsigned char* const vbufs[3] = {v_lds0, v_lds1, v_lds2};
+
+  int bh, qb;
+  decode_qblock(p, bh, qb);
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i32 = lane & 31, g = lane >> 5;
+  const int q0 = qb * kFwdBlockM;
+  const int wq0 = q0 + 32 * wave_u;
+  const int q_row = wq0 + i32;
+  const size_t base = (size_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
+  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
+
+  // Q and dO rows of this lane's query: the B operands of Sᵀ = K Qᵀ, dPᵀ = V dOᵀ.
+  bf16x8_t qf[T::KS], of[T::KS];
+  float2 ld;
+  {
+    const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc(p.q + base, N * T::ROW);
+    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(p.dout + base, N * T::ROW);
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(qrsrc, q_row * T::ROW + (2 * kk + g) * 16));
+      of[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(orsrc, q_row * T::ROW + (2 * kk + g) * 16));
+    }
+    ld = buffer_load8(make_rsrc(p.ld + (size_t)bh * N * 2, N * 8), q_row * 8);
+  }
+
+  TileReads<D> rd;
+  rd.init(lane);
+
+  const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
+  const int goff = run_goff<D>(wave_u % R, lane);
+  auto issue = [&](int j, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int toff = j * KT;  // byte offset of the tile's first row
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = wave_u + i * kFwdWaves;
+      if (x < R)
+        load_lds16(krsrc, kbufs[B] + x * 1024, goff + toff + (x - wave_u % R) * 1024);
+      else
+        load_lds16(vrsrc, vbufs[B] + (x - R) * 1024, goff + toff + (x - R - wave_u % R) * 1024);
+    }
+  };
+  auto wait_stage = [&](bool more) {
+    if (more)
+      wait_vmcnt<PER>();
+    else
+      wait_vmcnt<0>();
+  };
+
+  f32x16_t dq[T::DSUB];
+#pragma unroll
+  for (int ds = 0; ds < T::DSUB; ++ds) dq[ds] = f32x16_t{};
+  const float c = p.scale_log2;
+  const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;  // last key this row sees
+
+  auto step = [&](int j, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int kv0 = j * BN;
+    if (CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
+    const unsigned char* kb = kbufs[B];
+    const unsigned char* vb = vbufs[B];
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) s[sub] = dp[sub] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(kb, kk, sub), qf[kk], s[sub], 0, 0, 0);
+        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(vb, kk, sub), of[kk], dp[sub], 0, 0, 0);
+      }
+    const bool edge = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > wq0);
+    float dsr[32];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -ld.x));
+        if (edge && kv0 + sub * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > lim) e = 0.f;
+        dsr[16 * sub + r] = e * (dp[sub][r] - ld.y);
+      }
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      const bf16x8_t sb = pack8(dsr + 8 * kk);
+#pragma unroll
+      for (int ds = 0; ds < T::DSUB; ++ds)
+        dq[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(kb, ds, kk), sb, dq[ds], 0, 0, 0);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue(0, I0{});
+  if (n_tiles > 1) issue(1, I1{});
+  wait_stage(n_tiles > 1);
+#pragma unroll
+  for (int kk = 0; kk < T::KS; ++kk)
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[kk])), "v"(__builtin_bit_cast(u32x4_t, of[kk])));
+  asm volatile("" ::"v"(ld.x), "v"(ld.y));
+  auto body = [&](int j, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    wait_stage(j + 1 < n_tiles);
+    block_barrier();
+    if (j + 2 < n_tiles) issue(j + 2, std::integral_constant<int, (B + 2) % 3>{});
+    step(j, buf);
+  };
+  for (int j = 0; j < n_tiles; j += 3) {
+    body(j, I0{});
+    if (j + 1 < n_tiles) body(j + 1, I1{});
+    if (j + 2 < n_tiles) body(j + 2, I2{});
+  }
+
+  if (q_row < N) {
+    uint16_t* row = p.dq + base + (size_t)q_row * D;
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = ds * 32 + r4 * 8 + g * 4;
+        u32x2_t w;
+        w[0] = pack_bf16x2(dq[ds][4 * r4 + 0] * p.scale, dq[ds][4 * r4 + 1] * p.scale);
+        w[1] = pack_bf16x2(dq[ds][4 * r4 + 2] * p.scale, dq[ds][4 * r4 + 3] * p.scale);
+        *reinterpret_cast<u32x2_t*>(row + d0) = w;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const int rows_per_block = 256 / (D / 8);
+  const long long rows = (long long)p.BH * p.N;
+  hipLaunchKernelGGL((fa_bwd_prep_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
+                     0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int d, int causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
+  return causal ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
+}
+
+}  // namespace fa

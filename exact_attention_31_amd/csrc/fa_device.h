@@ -39,19 +39,24 @@ __device__ inline u32x2_t lds_tr_read(const unsigned char* base, int off) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// Range check of the buffer loads below: a lane whose vector offset (plus the
+// instruction's immediate offset) lies at or past num_records reads zeros.
+// Callers pass every variable offset as the vector offset and keep the scalar
+// offset at zero, since the range check is not specified to include it.
+
 // 4 bytes per lane from a buffer straight into LDS (buffer_load_dword ... lds):
-// lane L's bytes land at lds + 4·L; bytes past num_records read as zero.
-__device__ inline void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+// lane L's bytes land at lds + 4·L.
+__device__ inline void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
 // 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
-// lane L's bytes [voff + soff, +16) land at lds + 16·L (lds uniform across the
-// wavefront); bytes past the buffer's num_records read as zero.  Kept in a
+// lane L's bytes [voff, +16) land at lds + 16·L (lds uniform across the
+// wavefront).  Kept in a
 // non-template function: used directly inside the kernel template, the
 // builtin makes the host pass drop the kernel's launch stub.
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
 // Raw buffer descriptor over `bytes` bytes at `base` (word 3: 32-bit data, no swizzle).

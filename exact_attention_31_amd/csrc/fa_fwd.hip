@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int goff, int kv0, unsigned char* dst) {
     unsigned char* d = dst + (wave_u & 3) * 1024;
 #pragma unroll
-    for (int i = 0; i < 2 * T::LOADS; ++i) load_lds16(rsrc, d + i * (kFwdWaves / 2) * 1024, goff, (kv0 + i * RPL) * T::ROW);
+    for (int i = 0; i < 2 * T::LOADS; ++i) load_lds16(rsrc, d + i * (kFwdWaves / 2) * 1024, goff + (kv0 + i * RPL) * T::ROW);
   };
 
   // Operand-read lane offsets (bytes within a tile).

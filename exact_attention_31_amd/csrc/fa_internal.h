@@ -59,11 +59,38 @@ struct DecodeParams {
   float scale_log2;
 };
 
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* ld;         // workspace [BH, N] pairs (L·log2 e, D = dO·O)
+  int BH;
+  int N;
+  int n_qblk;        // query blocks of kFwdBlockM rows (dQ kernel)
+  int n_kblk;        // key blocks of kBwdBlockK keys (dK/dV kernel)
+  int xcd_remap_q;   // 1: group each head's blocks on one XCD
+  int xcd_remap_k;
+  float scale;
+  float scale_log2;
+};
+
+// dK/dV kernel: 4 wavefronts (one per SIMD) of 32 keys each.
+constexpr int kBwdKvWaves = 4;
+constexpr int kBwdKvThreads = 64 * kBwdKvWaves;
+constexpr int kBwdBlockK = 32 * kBwdKvWaves;
+
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
 // divides the group size g = Hq / Hkv.
 __host__ __device__ inline int decode_group_width(int g) { return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream);
 
 }  // namespace fa

@@ -1,7 +1,8 @@
 /* fa.h — C ABI of the exact-attention library for MI355X (gfx950).
  *
- * Two operations, both exact attention (the result of standard attention up to
- * rounding order), each returning the output O and the per-row log-sum-exp L:
+ * Exact attention (the result of standard attention up to rounding order):
+ * the forward and decode calls return the output O and the per-row
+ * log-sum-exp L; the backward call returns the gradients of Q, K and V:
  *
  *   fa_fwd     prefill: O = softmax(scale · Q Kᵀ [+ causal mask]) V, computed as
  *              one fused, tiled pass with an online softmax, so the N×N score
@@ -16,10 +17,14 @@
  *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5);
  *              fa_decode_gqa adds grouped query heads (several query heads per
  *              cached K/V head) and per-sequence key counts.
+ *   fa_bwd     backward of fa_fwd: dQ, dK, dV from the saved O and L, with
+ *              the probabilities recomputed rather than stored
+ *              ([15-779 L5] §7; [pinghaoyang FA-1] "Backward").
  *
  * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
  * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
- * 案例：Transformer、注意力与 FlashAttention" (CMU 15-779 lecture 5 notes).
+ * 案例：Transformer、注意力与 FlashAttention" (CMU 15-779 lecture 5 notes);
+ * [pinghaoyang FA-1] "FlashAttention 完全拆解（一）" (pinghaoyang.com.cn).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -53,7 +58,7 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = 3, /* head dimension other than 64 or 128                 */
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned               */
   FA_ERR_VALUE = 5,       /* scale not > 0 and finite, or num_splits outside [1, Lkv] */
-  FA_ERR_WORKSPACE = 6,   /* decode workspace missing or smaller than required   */
+  FA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
   FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch            */
   FA_ERR_ALIAS = 8        /* an output overlaps an input                         */
 } fa_status;
@@ -73,6 +78,34 @@ typedef enum fa_status {
  * that much), so the fp32 accumulation of weight·v cannot overflow. */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: fp32 pairs [B, H, N, 2].
+ * Returns 0 when the sizes are invalid. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/* Prefill backward: the gradients of the loss through O = fa_fwd(q, k, v).
+ *   q, k, v : bf16 [B, H, N, d], the forward's inputs.
+ *   o, lse  : the forward's outputs (bf16 [B, H, N, d] and fp32 [B, H, N]);
+ *             P is recomputed tile by tile as exp(scale·q_i·k_j − L_i), never
+ *             stored ([15-779 L5] §7.2), and D_i = dO_i · O_i is formed from o
+ *             once per row ([15-779 L5] §7.3).
+ *   dout    : bf16 [B, H, N, d], the gradient of the loss with respect to O.
+ *   dq, dk, dv : bf16 [B, H, N, d], written in full:
+ *             dV = Pᵀ dO,  dS = P ∘ (dO Vᵀ − D),  dQ = scale · dS K,
+ *             dK = scale · dSᵀ Q  ([15-779 L5] §7.1; [pinghaoyang FA-1]
+ *             "Backward").  Deterministic: the same inputs give the same bits.
+ *   scale, causal : as passed to fa_fwd.
+ *   workspace : device buffer of at least fa_bwd_workspace_bytes(B, H, N)
+ *             bytes, 16-byte aligned, owned by the caller; contents on entry
+ *             ignored, on exit unspecified; calls sharing it must be ordered.
+ * Three kernels run in stream order: the per-row (L, D) pass, then dK and dV
+ * (key blocks outside, query tiles inside, [15-779 L5] §7.4), then dQ (query
+ * blocks outside).  Errors as for fa_fwd; FA_ERR_WORKSPACE for a missing or
+ * short workspace; FA_ERR_ALIAS when an output or the workspace overlaps an
+ * input or another output.  B·H·N must stay below 2^31. */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fa_decode needs for these sizes: the per-split
  * partial results, fp32 [B, H, num_splits, d] then fp32 [B, H, num_splits].

@@ -29,7 +29,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
-                 "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version"):
+                 "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes"):
         assert want in names
 
 
@@ -53,7 +53,7 @@ def test_status_strings_and_version():
 
 # fake, 16-byte aligned, distinct "device" addresses: every call below must be
 # rejected by validation, so nothing ever dereferences them
-P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(6)]
+P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(10)]
 MISALIGNED = ctypes.c_void_p(0x10000008)
 
 
@@ -109,6 +109,29 @@ def test_decode_gqa_argument_checks():
     assert _gqa(wsb=need - 1) == 6
     assert _gqa(seqlens=ctypes.c_void_p(0x50000002)) == 4  # int32 lengths must be 4-byte aligned
     assert _gqa(seqlens=P[3]) == 8          # lengths inside the output
+
+
+def _bwd(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, N=16, d=64,
+         scale=0.125, causal=1, ws=P[9], wsb=1 << 20):
+    return _lib().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, ctypes.c_float(scale), causal, ws, wsb, None)
+
+
+def test_bwd_argument_checks():
+    assert _bwd(do=None) == 1 and _bwd(lse=None) == 1 and _bwd(dv=None) == 1
+    assert _bwd(B=0) == 2 and _bwd(N=0) == 2
+    assert _bwd(B=1 << 12, H=1 << 12, N=1 << 8) == 2       # B·H·N beyond 2^31 rows
+    assert _bwd(d=96) == 3
+    assert _bwd(scale=float("nan")) == 5 and _bwd(scale=0.0) == 5
+    assert _bwd(ws=None) == 6
+    need = _lib().fa_bwd_workspace_bytes(1, 2, 16)
+    assert need == 2 * 16 * 8                                # one (L, D) pair per row
+    assert _bwd(wsb=need - 1) == 6
+    assert _bwd(dk=MISALIGNED) == 4
+    assert _bwd(dq=P[0]) == 8                               # dQ on top of q
+    assert _bwd(dv=P[3]) == 8                               # dV on top of o
+    assert _bwd(dk=P[6]) == 8                               # two outputs on one buffer
+    assert _bwd(ws=ctypes.c_void_p(0x50000000 + 16)) == 8   # workspace inside dO's range
+    assert _lib().fa_bwd_workspace_bytes(0, 1, 1) == 0
 
 
 def test_tile_shape():
