@@ -13,6 +13,9 @@ Each call is also timed with HIP events recorded on the stream it runs on
   * roofline_decode  the decode pair against the HBM peak (8 TB/s)
   * decode_gqa       grouped-query decode (B16, 32 query heads over 8 K/V heads,
                      Lkv 32768, d128), timed on its own after the step
+  * backward         fa_bwd on the prefill workload (the step's O and L, a
+                     seeded dO), timed on its own after the step: TFLOP/s of
+                     the five N×N×d products, 10·N²·d·B·H / 2 (causal)
   * cpu_baseline     the fp64 oracle on a bounded sample of the same workload,
                      on this host's cores (rank 0, N=1 only)
 Prints one JSON line.
@@ -38,10 +41,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "copy"], default="all",
                     help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
-                         "decode measured after the step; 'copy' times a plain 1 GiB device-to-device "
-                         "copy, the reference for scaling HBM byte counters")
+                         "decode and 'bwd' the backward, both measured after the step; 'copy' times a "
+                         "plain 1 GiB device-to-device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -218,6 +221,33 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
             "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
 
 
+def time_bwd(torch, fa, synth, dev, args, wf, q, k, v):
+    """The backward on the prefill workload, timed on its own: the forward's O and L
+    and a seeded dO, W warm-up calls, then K calls, each between HIP events."""
+    print(f"[bench] backward: {wf.name}", file=sys.stderr, flush=True)
+    do = synth.make_prefill_grad(wf).to(dev)
+    o, lse = fa.fa_fwd(q, k, v, scale=wf.scale, causal=wf.causal)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(wf.B, wf.H, wf.N), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        fa.fa_bwd(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record()
+        fa.fa_bwd(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    avg = sum(ms) / len(ms)
+    flops = synth.bwd_flops(wf)
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(avg, 4),
+            "ms_min": round(min(ms), 4), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": flops,
+            "note": "three kernels per call (per-row L and D; dK, dV; dQ); the dQ pass recomputes S and dP, "
+                    "so the matrix cores run 7/5 of the counted FLOPs"}
+
+
 def main():
     args = parse()
     if args.make_traffic:
@@ -247,7 +277,7 @@ def main():
     do_d = args.only in ("all", "decode")
     print(f"[bench] generating inputs: {wf.name}, {wd.name}", file=sys.stderr, flush=True)
     q = k = v = o = lse = qd = kd = vd = ws = None
-    if do_f or args.only == "all":
+    if do_f or args.only in ("all", "bwd"):
         q, k, v = (t.to(dev) for t in synth.make_prefill(wf))
         o = torch.empty_like(q)
         lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device=dev)
@@ -337,6 +367,8 @@ def main():
                                   "traffic": traffic_bytes(traffic, "decode"), "algorithmic_bytes": dbytes}
     if args.only in ("all", "gqa"):
         out["decode_gqa"] = time_gqa(torch, fa, synth, dev, args, traffic)
+    if args.only in ("all", "bwd"):
+        out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v)
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)
