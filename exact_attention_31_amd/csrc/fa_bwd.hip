@@ -255,56 +255,133 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   for (int ds = 0; ds < T::DSUB; ++ds) dk[ds] = dv[ds] = f32x16_t{};
   const float c = p.scale_log2;
 
-  auto step = [&](int s, auto buf) __attribute__((always_inline)) {
-    constexpr int B = decltype(buf)::value;
-    const int qs0 = (first + s) * BM;
-    if (CAUSAL && qs0 + BM - 1 < kw) return;  // every query of the tile precedes this wavefront's keys
-    const unsigned char* qb = qbufs[B];
-    const unsigned char* ob = obufs[B];
-    f32x16_t sacc[2], dpacc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) sacc[u] = dpacc[u] = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < T::KS; ++kk)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(qb, kk, u), kf[kk], sacc[u], 0, 0, 0);
-        dpacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(ob, kk, u), vf[kk], dpacc[u], 0, 0, 0);
-      }
-    const bool diag = CAUSAL && qs0 < kw + 32;  // some query of the tile precedes some key
-    const float* lb = lbufs[B];
-    float pr[32], dsr[32];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
+  // One step = the 64 query rows of a stage, as two 32-row sub-tiles u, in
+  // four phases of 2·d/16 MFMAs each:
+  //   A  S(0), dP(0)                     (S = Q Kᵀ, dP = dO Vᵀ; Q, dO rows from LDS)
+  //   B  S(1), dP(1)   + softmax of u = 0 (P, dS as bf16 operands)
+  //   C  dV, dK(0)     + softmax of u = 1 (dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS; transpose reads)
+  //   D  dV, dK(1)
+  // With one wavefront per SIMD nothing else hides latency, so the order is
+  // fixed by hand: each MFMA is followed by the LDS read of the operand it
+  // needs LA (or LC) MFMAs later and by one element of the vector work, and
+  // a scheduling fence after each such group keeps the compiler from
+  // regrouping them.
+  constexpr int LA = 6;  // 16-byte operand reads in flight in phases A and B
+  constexpr int LC = 4;  // transpose-read operands in flight in phases C and D
+  constexpr int NA = 2 * T::KS;    // MFMAs per sub-tile in A and B (S and dP, KS k-steps each)
+  constexpr int NC = 4 * T::DSUB;  // MFMAs per sub-tile in C and D (dV and dK, 2 k-steps × DSUB)
+  static_assert(16 % NA == 0 && 16 % NC == 0 && LA <= NA && LC <= NC, "phase shapes");
+  f32x16_t sacc[2], dpacc[2];
+  u32x4_t pw[4], sw[4];  // bf16 P and dS: the B operands of the four k-steps
+  auto step_body = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, int qs0,
+                       auto masked) __attribute__((always_inline)) {
+    // operand j of A/B: sub-tile j / NA, k-step (j % NA) / 2, Q (even j) or dO (odd j)
+    auto op_a = [&](int j) __attribute__((always_inline)) {
+      return rd.rows((j & 1) ? ob : qb, (j % NA) >> 1, j / NA);
+    };
+    auto mfma_a = [&](int j, bf16x8_t a) __attribute__((always_inline)) {
+      const int u = j / NA, kk = (j % NA) >> 1;
+      if (j & 1)
+        dpacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[kk], dpacc[u], 0, 0, 0);
+      else
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], sacc[u], 0, 0, 0);
+    };
+    // operand m of C/D: sub-tile u = m / NC, k-step 2u + (m % NC) / (2·DSUB),
+    // d sub-tile (m / 2) % DSUB, dO for dV (even m) or Q for dK (odd m)
+    auto op_c = [&](int m) __attribute__((always_inline)) {
+      return rd.tr((m & 1) ? qb : ob, (m >> 1) % T::DSUB, 2 * (m / NC) + (m % NC) / (2 * T::DSUB));
+    };
+    auto mfma_c = [&](int m, bf16x8_t a) __attribute__((always_inline)) {
+      const int kk = 2 * (m / NC) + (m % NC) / (2 * T::DSUB), ds = (m >> 1) % T::DSUB;
+      if (m & 1)
+        dk[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, sw[kk]), dk[ds], 0, 0, 0);
+      else
+        dv[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pw[kk]), dv[ds], 0, 0, 0);
+    };
+    float4 ldq[2][8];  // (L·log2 e, D) of rows 32u + 8t + 4g + (0..3): t-th pair of float4
+    auto read_ld = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        // (L·log2 e, D) of accumulator rows 32u + 8t + 4g + (0..3)
-        const float4 a = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g));
-        const float4 b = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g + 2));
-        const float l2[4] = {a.x, a.z, b.x, b.z}, dd[4] = {a.y, a.w, b.y, b.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * t + i;
-          float e = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], c, -l2[i]));
-          if (diag && key > qs0 + 32 * u + 8 * t + 4 * g + i) e = 0.f;
-          pr[16 * u + r] = e;
-          dsr[16 * u + r] = e * (dpacc[u][r] - dd[i]);
-        }
+        ldq[u][2 * t] = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g));
+        ldq[u][2 * t + 1] = *reinterpret_cast<const float4*>(lb + 2 * (32 * u + 8 * t + 4 * g + 2));
       }
-#pragma unroll
-    for (int kk = 0; kk < BM / 16; ++kk) {
-      const bf16x8_t pb = pack8(pr + 8 * kk), sb = pack8(dsr + 8 * kk);
-#pragma unroll
-      for (int ds = 0; ds < T::DSUB; ++ds) {
-        dv[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(ob, ds, kk), pb, dv[ds], 0, 0, 0);
-        dk[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(qb, ds, kk), sb, dk[ds], 0, 0, 0);
+    };
+    float pr[2], dsr[2];
+    // element r of sub-tile u (accumulator row 32u + 8(r/4) + 4g + r%4)
+    auto soft_el = [&](int u, int r) __attribute__((always_inline)) {
+      const float4 q4 = ldq[u][2 * (r >> 2) + ((r >> 1) & 1)];
+      const float l2 = (r & 1) ? q4.z : q4.x, dd = (r & 1) ? q4.w : q4.y;
+      float e = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], c, -l2));
+      if (decltype(masked)::value && key > qs0 + 32 * u + 8 * (r >> 2) + 4 * g + (r & 3)) e = 0.f;
+      pr[r & 1] = e;
+      dsr[r & 1] = e * (dpacc[u][r] - dd);
+      if (r & 1) {
+        pw[2 * u + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pr[0], pr[1]);
+        sw[2 * u + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsr[0], dsr[1]);
       }
+    };
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sacc[u] = dpacc[u] = f32x16_t{};
+    bf16x8_t ra[LA], rc[LC];
+    read_ld(0);
+#pragma unroll
+    for (int j = 0; j < LA; ++j) ra[j] = op_a(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {  // A
+      mfma_a(j, ra[j % LA]);
+      ra[j % LA] = op_a(j + LA);
+      if (j == NA - 1) read_ld(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = NA; j < 2 * NA; ++j) {  // B
+      mfma_a(j, ra[j % LA]);
+      if (j + LA < 2 * NA)
+        ra[j % LA] = op_a(j + LA);
+      else if (j + LA - 2 * NA < LC)
+        rc[j + LA - 2 * NA] = op_c(j + LA - 2 * NA);
+#pragma unroll
+      for (int r = (j - NA) * (16 / NA); r < (j - NA + 1) * (16 / NA); ++r) soft_el(0, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {  // C
+      mfma_c(m, rc[m % LC]);
+      rc[m % LC] = op_c(m + LC);
+#pragma unroll
+      for (int r = m * (16 / NC); r < (m + 1) * (16 / NC); ++r) soft_el(1, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = NC; m < 2 * NC; ++m) {  // D
+      mfma_c(m, rc[m % LC]);
+      if (m + LC < 2 * NC) rc[m % LC] = op_c(m + LC);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // CLEAN: every query of the step comes at or after every key of the block.
+  auto step = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int qs0 = (first + s) * BM;
+    // lane offsets opaque here: addresses are formed as offset + constant
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) asm volatile("" : "+v"(rd.row[kk]));
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(rd.tr0[ds]), "+v"(rd.tr8[ds]));
+    if (decltype(clean)::value) {
+      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::false_type{});
+    } else if (qs0 + BM - 1 >= kw) {  // else every query of the step precedes this wavefront's keys
+      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::true_type{});
     }
   };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using Y = std::true_type;
+  using G = std::false_type;
   issue(0, I0{});
   if (n_steps > 1) issue(1, I1{});
   wait_stage(n_steps > 1);
@@ -313,17 +390,31 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
 #pragma unroll
   for (int kk = 0; kk < T::KS; ++kk)
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, kf[kk])), "v"(__builtin_bit_cast(u32x4_t, vf[kk])));
-  auto body = [&](int s, auto buf) __attribute__((always_inline)) {
+  auto body = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     wait_stage(s + 1 < n_steps);
     block_barrier();  // stage s is in LDS for everyone; stage s-1's buffers are free
     if (s + 2 < n_steps) issue(s + 2, std::integral_constant<int, (B + 2) % 3>{});
-    step(s, buf);
+    step(s, buf, clean);
   };
-  for (int s = 0; s < n_steps; s += 3) {
-    body(s, I0{});
-    if (s + 1 < n_steps) body(s + 1, I1{});
-    if (s + 2 < n_steps) body(s + 2, I2{});
+  auto loop = [&](int s0, auto phase) __attribute__((always_inline)) {
+    constexpr int P = decltype(phase)::value;  // s0 mod 3
+    for (int s = s0; s < n_steps; s += 3) {
+      body(s, phase, Y{});
+      if (s + 1 < n_steps) body(s + 1, std::integral_constant<int, (P + 1) % 3>{}, Y{});
+      if (s + 2 < n_steps) body(s + 2, std::integral_constant<int, (P + 2) % 3>{}, Y{});
+    }
+  };
+  if constexpr (CAUSAL) {
+    // The block's keys are 128 from a multiple of 128, its steps 64 queries
+    // from the first key on: the first two steps hold the diagonal (masked),
+    // and from the third on every query follows every key of the block.
+    static_assert(kBwdBlockK == 2 * BM, "two diagonal steps");
+    body(0, I0{}, G{});
+    if (n_steps > 1) body(1, I1{}, G{});
+    loop(2, I2{});
+  } else {
+    loop(0, I0{});
   }
 
   // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, one store each ------------------
