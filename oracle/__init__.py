@@ -27,6 +27,7 @@ from .ref import (
     decode_ref,
     decode_gqa_ref,
     attention_bwd_ref,
+    attention_block_sparse_ref,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode, bwd_allowance, check_bwd
 
@@ -37,6 +38,7 @@ __all__ = [
     "decode_ref",
     "decode_gqa_ref",
     "attention_bwd_ref",
+    "attention_block_sparse_ref",
     "bf16_half_ulp",
     "o_excess",
     "check_prefill",

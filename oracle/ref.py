@@ -160,6 +160,43 @@ def decode_gqa_ref(q, k, v, scale, seqlens=None):
     return o, lse
 
 
+def attention_block_sparse_ref(q, k, v, scale, causal, block_mask, block=128, rows=None):
+    """Block-sparse attention ([FA-1拆解] "块稀疏扩展"): standard attention in which
+    every score whose (query block, key block) is switched off in the block
+    mask is masked like a causal one, i.e. set to −∞ before the softmax.
+
+    block_mask: [T_q, T_k] or [B·H, T_q, T_k] array of 0/1 over blocks of
+    ``block`` query rows × ``block`` keys (T_q = T_k = ⌈N/block⌉), one mask for
+    all heads or one per (b, h) in b-major order.  Combined with the causal
+    mask when ``causal``.  A row left with no key at all has no softmax; its
+    output is taken as O = 0 and L = −∞ (the empty sum: ℓ = 0, ln ℓ = −∞).
+    Returns (O, LSE) as ``attention_ref`` does.
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    B, H, N, _ = q.shape
+    mask = np.asarray(block_mask)
+    if rows is None:
+        rows = np.arange(N)
+    rows = np.asarray(rows)
+    keys = np.arange(N)
+    o = np.empty((B, H, rows.size, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, rows.size), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            mk = mask if mask.ndim == 2 else mask[b * H + h]
+            s = scores(q[b, h][rows], k[b, h], scale, causal, rows)
+            on = mk[rows[:, None] // block, keys[None, :] // block] != 0
+            s = np.where(on, s, -np.inf)
+            empty = np.all(np.isneginf(s), axis=1)
+            s_safe = np.where(empty[:, None], 0.0, s)  # any finite row: its result is discarded below
+            p, m, l = safe_softmax(s_safe)
+            o[b, h] = np.where(empty[:, None], 0.0, p @ v[b, h])
+            lse[b, h] = np.where(empty, -np.inf, m + np.log(l))
+    return o, lse
+
+
 def attention_bwd_ref(q, k, v, do, scale, causal, o=None):
     """Exact attention backward: the gradients of Σ dO ∘ O with respect to Q, K, V.
 

@@ -17,7 +17,8 @@ import numpy as np
 import pytest
 import scipy.special
 
-from oracle import attention_bwd_ref, attention_ref, decode_gqa_ref, decode_ref, safe_softmax, scores
+from oracle import (attention_block_sparse_ref, attention_bwd_ref, attention_ref, decode_gqa_ref, decode_ref,
+                    safe_softmax, scores)
 from oracle.compare import bf16_half_ulp, bf16_rne, bwd_allowance, check_bwd, check_prefill
 import _method_fp64 as M
 
@@ -475,6 +476,73 @@ def test_bf16_rounding_helpers():
     assert r["pass"] and r["floor"] > 0
     r = check_prefill(x + 0.02, [0.0], x, [0.0])
     assert not r["ok"]
+
+
+# --------------------------------------------------------------------------
+# block-sparse attention ([FA-1拆解] "块稀疏扩展")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_all_ones_is_dense(causal):
+    q, k, v = (_rand((1, 2, 70, 8), 61 + i) for i in range(3))
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, causal, np.ones((3, 3)), block=32)
+    ro, rl = attention_ref(q, k, v, 0.3, causal)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-13)
+
+
+def test_block_sparse_lower_triangle_with_causal_is_causal():
+    """Blocks wholly above the diagonal hold only keys after every query of the
+    block, so switching them off changes nothing under the causal mask."""
+    q, k, v = (_rand((1, 1, 100, 8), 64 + i) for i in range(3))
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, True, np.tril(np.ones((4, 4))), block=32)
+    ro, rl = attention_ref(q, k, v, 0.3, True)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-13)
+
+
+def test_block_sparse_block_diagonal_is_independent_blocks():
+    q, k, v = (_rand((2, 1, 90, 8), 67 + i) for i in range(3))
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, False, np.eye(3), block=32)
+    for lo, hi in ((0, 32), (32, 64), (64, 90)):
+        ro, rl = attention_ref(q[:, :, lo:hi], k[:, :, lo:hi], v[:, :, lo:hi], 0.3, False)
+        np.testing.assert_allclose(o[:, :, lo:hi], ro, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l[:, :, lo:hi], rl, rtol=0, atol=1e-13)
+
+
+def test_block_sparse_dropped_key_blocks_are_gone():
+    """Switching key block j off for every query block equals attention over the
+    remaining keys; with causal, query rows keep their own positions."""
+    q, k, v = (_rand((1, 1, 96, 8), 70 + i) for i in range(3))
+    mask = np.ones((3, 3))
+    mask[:, 1] = 0
+    keep = np.r_[0:32, 64:96]
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, False, mask, block=32)
+    ro, rl = attention_ref(q, k[:, :, keep], v[:, :, keep], 0.3, False)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-13)
+
+
+def test_block_sparse_empty_rows_and_per_head_masks():
+    q, k, v = (_rand((1, 2, 64, 8), 73 + i) for i in range(3))
+    m0 = np.array([[1, 0], [0, 0]])   # head 0: the second query block sees nothing
+    m1 = np.array([[0, 1], [1, 1]])   # head 1: the first query block sees only key block 1
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, False, np.stack([m0, m1]), block=32)
+    assert np.all(o[0, 0, 32:] == 0) and np.all(np.isneginf(l[0, 0, 32:]))
+    o0, l0 = attention_block_sparse_ref(q[:, :1], k[:, :1], v[:, :1], 0.3, False, m0, block=32)
+    np.testing.assert_array_equal(o[:, :1], o0)
+    ro, rl = attention_ref(q[:, 1:, :32], k[:, 1:, 32:], v[:, 1:, 32:], 0.3, False)
+    np.testing.assert_allclose(o[:, 1:, :32], ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l[:, 1:, :32], rl, rtol=0, atol=1e-13)
+    # causal + a mask that leaves the first rows of a block without keys
+    o, l = attention_block_sparse_ref(q, k, v, 0.3, True, np.array([[0, 0], [1, 1]]), block=32)
+    assert np.all(o[0, :, :32] == 0) and np.all(np.isneginf(l[0, :, :32]))
+    ro, rl = attention_ref(q, k, v, 0.3, True, rows=np.arange(32, 64))
+    np.testing.assert_allclose(o[:, :, 32:], ro, rtol=0, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
