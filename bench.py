@@ -13,6 +13,10 @@ Each call is also timed with HIP events recorded on the stream it runs on
   * roofline_decode  the decode pair against the HBM peak (8 TB/s)
   * decode_gqa       grouped-query decode (B16, 32 query heads over 8 K/V heads,
                      Lkv 32768, d128), timed on its own after the step
+  * block_sparse     fa_fwd_block_sparse on B1 H16 N16384 d128 with a seeded
+                     block mask (own and first key block, 10 % of the rest),
+                     against fa_fwd on the same inputs: TFLOP/s of the kept
+                     blocks and the speed-up over the dense call
   * backward         fa_bwd on the prefill workload (the step's O and L, a
                      seeded dO), timed on its own after the step: TFLOP/s of
                      the five N×N×d products, 10·N²·d·B·H / 2 (causal)
@@ -41,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "sparse", "copy"], default="all",
                     help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
                          "decode and 'bwd' the backward, both measured after the step; 'copy' times a "
                          "plain 1 GiB device-to-device copy, the reference for scaling HBM byte counters")
@@ -221,6 +225,40 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
             "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
 
 
+def time_sparse(torch, fa, synth, dev, args):
+    """Block-sparse forward against the dense forward on the long workload, each timed
+    W + K calls between HIP events, interleaved."""
+    ws_ = synth.BY_NAME["long_noncausal_b1h16n16384d128"]
+    print(f"[bench] block sparse: {ws_.name}", file=sys.stderr, flush=True)
+    q, k, v = (t.to(dev) for t in synth.make_prefill(ws_))
+    mask = synth.make_block_mask(ws_, 0.1)
+    md = mask.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((ws_.B, ws_.H, ws_.N), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        fa.fa_fwd_block_sparse(q, k, v, md, scale=ws_.scale, out=o, lse=lse)
+        fa.fa_fwd(q, k, v, scale=ws_.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        fa.fa_fwd_block_sparse(q, k, v, md, scale=ws_.scale, out=o, lse=lse)
+        e[1].record()
+        e[2].record()
+        fa.fa_fwd(q, k, v, scale=ws_.scale, out=o, lse=lse)
+        e[3].record()
+    torch.cuda.synchronize()
+    sp = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    dn = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev)
+    flops = synth.block_sparse_flops(ws_, mask)
+    kept = float(mask.float().mean())
+    tf = flops / (sp * 1e-3) / 1e12
+    return {"workload": ws_.name + "_blocksparse", "mask": "own + first key block, 10 % of the rest (seeded)",
+            "kept_blocks": round(kept, 4), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(sp, 4),
+            "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "dense_ms": round(dn, 4),
+            "speedup_vs_dense": round(dn / sp, 2), "ideal_speedup": round(1 / kept, 2), "algorithmic_flops": flops}
+
+
 def time_bwd(torch, fa, synth, dev, args, wf, q, k, v):
     """The backward on the prefill workload, timed on its own: the forward's O and L
     and a seeded dO, W warm-up calls, then K calls, each between HIP events."""
@@ -369,6 +407,8 @@ def main():
         out["decode_gqa"] = time_gqa(torch, fa, synth, dev, args, traffic)
     if args.only in ("all", "bwd"):
         out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v)
+    if args.only in ("all", "sparse"):
+        out["block_sparse"] = time_sparse(torch, fa, synth, dev, args)
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)

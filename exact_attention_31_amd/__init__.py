@@ -10,6 +10,7 @@ library is missing or fails to load, the calls raise.
     fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
     fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None) -> (o, lse)
     fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
+    fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False) -> (o, lse)
     fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, N)                  -> int
     fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
@@ -56,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode.restype = i
     lib.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, vp, sz, vp]
     lib.fa_decode_gqa.restype = i
+    lib.fa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_fwd_block_sparse.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -150,6 +153,46 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
                                B, H, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+SPARSE_BLOCK = 128
+
+
+def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None):
+    """Block-sparse prefill: fa_fwd with the score blocks whose mask entry is zero set
+    to −∞ and skipped.  ``block_mask``: uint8 (or bool) [T, T] or [B·H, T, T] on q's
+    device, T = ⌈N/128⌉.  Rows left with no key get O = 0 and LSE = −∞."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ")
+    B, H, N, d = q.shape
+    T = -(-N // SPARSE_BLOCK)
+    m = block_mask
+    if not isinstance(m, torch.Tensor) or m.device != q.device:
+        raise ValueError("block_mask must be a tensor on q's device")
+    if m.dtype == torch.bool:
+        m = m.to(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise TypeError("block_mask must be uint8 or bool")
+    if m.dim() == 2:
+        m = m.unsqueeze(0)
+    if m.dim() != 3 or m.shape[1:] != (T, T) or m.shape[0] not in (1, B * H):
+        raise ValueError(f"block_mask must be [T, T] or [B*H, T, T] with T = {T}, got {tuple(block_mask.shape)}")
+    m = m.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load_library().fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                            B, H, N, d, float(scale), int(bool(causal)), m.data_ptr(), m.shape[0],
+                                            _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_block_sparse")
     return out, lse
 
 

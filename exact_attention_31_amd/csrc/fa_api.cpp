@@ -66,14 +66,18 @@ long long fa_fwd_tile_pairs(int N, int d, int causal) {
   return pairs;
 }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                 int d, float scale, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const unsigned char* block_mask, int mask_heads, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const size_t elems = count4(B, H, N, d);
   // one head's K (and V) is addressed through a buffer descriptor of N·d·2 bytes
-  if (elems == 0 || (unsigned long long)N * d * 2 > 0x7fffffffull || (unsigned long long)B * H > (1ull << 24) ||
+  if (elems == 0 || (unsigned long long)N * d * 2 > 0x7fff0000ull || (unsigned long long)B * H > (1ull << 24) ||
       (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
     return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
@@ -82,6 +86,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(lse, lb, q, tb) ||
       overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) || overlap(o, tb, lse, lb))
     return FA_ERR_ALIAS;
+  const int nb = fa::ceil_div(N, fa::kSparseBlock);
+  if (block_mask) {
+    if (nb > fa::kSparseMaxBlocks) return FA_ERR_SHAPE;
+    if (mask_heads != 1 && mask_heads != B * H) return FA_ERR_SHAPE;
+    const size_t mb = (size_t)mask_heads * nb * nb;
+    if (overlap(o, tb, block_mask, mb) || overlap(lse, lb, block_mask, mb)) return FA_ERR_ALIAS;
+  }
 
   fa::FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -96,8 +107,28 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.xcd_remap = (total % 8 == 0) && ((total / 8) % p.n_qblk == 0);
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
+  p.block_mask = block_mask;
+  p.mask_heads = mask_heads;
+  p.mask_tq = nb;
+  p.mask_tk = nb;
   if (fa::launch_fwd(p, d, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 int d, float scale, int causal, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, 0, stream);
+}
+
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                              int d, float scale, int causal, const unsigned char* block_mask, int mask_heads,
+                              void* stream) {
+  if (!block_mask) return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_heads, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {

@@ -123,15 +123,24 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
   }
 }
 
-template <int D, bool CAUSAL>
+// SPARSE: block-sparse attention ([FA-1拆解] "块稀疏扩展"): a mask over blocks
+// of kSparseBlock query rows × kSparseBlock keys switches whole score blocks
+// off.  The workgroup lists the key blocks either of its two query blocks
+// keeps and streams only those; a wavefront treats a listed key tile its own
+// query block does not keep like a tile above the diagonal (never visited).
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
+  static_assert(kSparseBlock == 2 * T::BN && kFwdBlockM == 2 * kSparseBlock, "two tiles per key block, two query blocks per workgroup");
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES],
       k_lds2[T::TILE_BYTES], k_lds3[T::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES],
       v_lds2[T::TILE_BYTES], v_lds3[T::TILE_BYTES];
   unsigned char* const kbufs[4] = {k_lds0, k_lds1, k_lds2, k_lds3};
   unsigned char* const vbufs[4] = {v_lds0, v_lds1, v_lds2, v_lds3};
+  // SPARSE: the kept key blocks, bits 0-13 the block, bit 14 (15) set when the
+  // first (second) query block of the workgroup keeps it
+  __shared__ uint16_t kblocks[SPARSE ? kSparseMaxBlocks : 1];
 
   int bh, qb;
   decode_work(p, bh, qb);
@@ -192,9 +201,50 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
-  const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
+  int n_tiles;
+  if constexpr (SPARSE) {
+    // wavefront 0 compacts the kept key blocks of the two query blocks into
+    // kblocks (ballot + running count); causal: none past the block's last row
+    const int rb0 = q0 / kSparseBlock;
+    const bool two = rb0 + 1 < p.mask_tq;
+    const uint8_t* m0 = p.block_mask + ((size_t)(p.mask_heads == 1 ? 0 : bh) * p.mask_tq + rb0) * p.mask_tk;
+    const int kb_end = CAUSAL ? min(p.mask_tk, ceil_div(min(N, q0 + kFwdBlockM), kSparseBlock)) : p.mask_tk;
+    int count = 0;
+    if (wave_u == 0) {
+      for (int base0 = 0; base0 < kb_end; base0 += 64) {
+        const int kbk = base0 + lane;
+        const int b0 = kbk < kb_end ? (m0[kbk] != 0) : 0;
+        const int b1 = (kbk < kb_end && two) ? (m0[p.mask_tk + kbk] != 0) : 0;
+        const uint64_t keep = __ballot(b0 | b1);
+        const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0));
+        if (b0 | b1) kblocks[pos] = (uint16_t)(kbk | (b0 << 14) | (b1 << 15));
+        count += __popcll(keep);
+      }
+    }
+    __shared__ int kblock_count;
+    if (tid == 0) kblock_count = count;
+    __syncthreads();
+    n_tiles = 2 * __builtin_amdgcn_readfirstlane(kblock_count);
+  } else {
+    n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
+  }
+  // first key of tile j (SPARSE: of the j-th tile of the kept blocks)
+  auto tile_kv0 = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE)
+      return (((int)kblocks[j >> 1] & 0x3fff) * kSparseBlock) + (j & 1) * T::BN;
+    else
+      return j * T::BN;
+  };
   const float c = p.scale_log2;
-  auto active = [&](int j) { return !CAUSAL || j * T::BN <= wq0 + 31; };  // some row of the wave sees the tile
+  auto active = [&](int j) __attribute__((always_inline)) {  // some row of the wave sees the tile
+    if constexpr (SPARSE) {
+      if (j >= n_tiles) return false;
+      const int e = __builtin_amdgcn_readfirstlane(kblocks[j >> 1]);
+      return ((e >> (14 + (wave_u >> 2))) & 1) && (!CAUSAL || tile_kv0(j) <= wq0 + 31);
+    } else {
+      return !CAUSAL || j * T::BN <= wq0 + 31;
+    }
+  };
 
   float m = -INFINITY;  // reference max of the raw logits q·k (this lane's query row)
   // Two running sums over this lane's half of the keys: ℓ of the fp32 P̃ (for
@@ -210,7 +260,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
 
   // ---- softmax phase of tile j: mask, row max, rescale, P̃ and the sums ------------
   auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
-    const int kv0 = j * T::BN;
+    const int kv0 = __builtin_amdgcn_readfirstlane(tile_kv0(j));
     if (!decltype(clean)::value && ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0))) {
       const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 #pragma unroll
@@ -227,7 +277,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float rs, rsb;
     auto exps = [&]() __attribute__((always_inline)) {
-      const float mc = m * c;
+      // SPARSE: a row may still have no key (m = −∞); 0 then stands in for
+      // the offset, which keeps masked logits at weight 0 instead of NaN
+      const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
       float r2[2] = {0.f, 0.f}, rb2[2] = {0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < T::KS_PV; ++kk) {
@@ -250,7 +302,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       rsb = rb2[0] + rb2[1];
     };
     exps();
-    if (__any(!(rs <= kSumBound))) {  // also taken for inf / NaN sums (first tile: m = -inf)
+    if (__any(!(rs <= kSumBound) || (SPARSE && m == -INFINITY))) {  // also taken for inf / NaN sums (first tile: m = -inf)
       // row max: four independent chains, then across the two lane halves
       float mx[4];
 #pragma unroll
@@ -264,7 +316,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       // the first tile holds key 0, visible to every row, so m is finite after it
       if (__any((mt - m) * c > kRescaleLog2)) {
         const float m_new = fmaxf(m, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+        const float alpha = (SPARSE && m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
         l *= alpha;
         lb *= alpha;
 #pragma unroll
@@ -364,14 +416,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   };
   auto issue_batch = [&](int b, auto phase) __attribute__((always_inline)) {
     constexpr int P = decltype(phase)::value;  // b mod 4
-    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(P));
-    if (b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(P + 3));
+    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 4)), kb(P));
+    if (b + 3 < n_tiles) load_tile(vrsrc, v_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 3)), vb(P + 3));
   };
   if (grp == 1) {
 #pragma unroll
     for (int b = -4; b < 0; ++b) {
-      if (b + 4 < n_tiles) load_tile(krsrc, k_goff, (b + 4) * T::BN, kb(b + 4));
-      if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, (b + 3) * T::BN, vb(b + 3));
+      if (b + 4 < n_tiles) load_tile(krsrc, k_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 4)), kb(b + 4));
+      if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 3)), vb(b + 3));
     }
   }
   wait_batches(batch_tiles(-3) + batch_tiles(-2) + batch_tiles(-1));
@@ -412,7 +464,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   using G = std::false_type;
   // Tiles 0 .. n_clean-1 are seen whole by every row of the workgroup;
   // iteration j is clean when tiles j and j+1 are.
-  const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  const int n_clean = SPARSE ? 0 : CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
   int j = 0;
   for (; j + 4 <= n_clean - 1; j += 4) {
     iter(j, I0{}, Y{});
@@ -432,7 +484,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   l = pair_sum(l);
   lb = pair_sum(lb);
   if (q_row < N) {
-    const float inv = 1.f / lb;
+    const float inv = (SPARSE && lb == 0.f) ? 0.f : 1.f / lb;  // SPARSE: a row with no key writes O = 0, L = −∞
     uint16_t* orow = p.o + base + (size_t)q_row * D;
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds)
@@ -448,22 +500,32 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  using T = Tile<D>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - T::LDS_BYTES);
+  // static LDS above 64 KiB: allow the kernel the CU's 160 KiB in all
+  static const hipError_t attr = [] {
+    const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, SPARSE>);
+    hipFuncAttributes fa_attr;
+    const hipError_t e = hipFuncGetAttributes(&fa_attr, fn);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (int)fa_attr.sharedSizeBytes);
+  }();
   if (attr != hipSuccess) return attr;
   const dim3 grid(p.BH * p.n_qblk);
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, dim3(kFwdThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, SPARSE>), grid, dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t launch_fwd_s(const FwdParams& p, int d, int causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_fwd_t<64, true, SPARSE>(p, stream) : launch_fwd_t<64, false, SPARSE>(p, stream);
+  return causal ? launch_fwd_t<128, true, SPARSE>(p, stream) : launch_fwd_t<128, false, SPARSE>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
-  return causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
+  return p.block_mask ? launch_fwd_s<true>(p, d, causal, stream) : launch_fwd_s<false>(p, d, causal, stream);
 }
 
 }  // namespace fa

@@ -39,7 +39,16 @@ struct FwdParams {
   int xcd_remap;     // 1: group each head's query blocks on one XCD
   float scale;       // softmax scale (for the LSE)
   float scale_log2;  // scale · log2(e): logits go straight into exp2
+  const uint8_t* block_mask;  // null: dense; else [mask_heads, mask_tq, mask_tk] block mask
+  int mask_heads;    // 1 (one mask for every head) or BH
+  int mask_tq;       // ⌈N / kSparseBlock⌉ query blocks
+  int mask_tk;       // ⌈N / kSparseBlock⌉ key blocks
 };
+
+// Block-sparse attention: mask blocks of kSparseBlock query rows × keys; at
+// most kSparseMaxBlocks key blocks (N ≤ 131072).
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 1024;
 
 struct DecodeParams {
   const uint16_t* q;

@@ -17,6 +17,9 @@
  *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5);
  *              fa_decode_gqa adds grouped query heads (several query heads per
  *              cached K/V head) and per-sequence key counts.
+ *   fa_fwd_block_sparse  fa_fwd with blocks of the score matrix switched off
+ *              by a block mask, their work and K/V traffic skipped
+ *              ([FA-1拆解] "块稀疏扩展").
  *   fa_bwd     backward of fa_fwd: dQ, dK, dV from the saved O and L, with
  *              the probabilities recomputed rather than stored
  *              ([15-779 L5] §7; [pinghaoyang FA-1] "Backward").
@@ -78,6 +81,27 @@ typedef enum fa_status {
  * that much), so the fp32 accumulation of weight·v cannot overflow. */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Query rows and keys per block of the fa_fwd_block_sparse mask. */
+#define FA_SPARSE_BLOCK 128
+
+/* Block-sparse prefill forward ([FA-1拆解] "块稀疏扩展"): fa_fwd with whole
+ * blocks of the score matrix switched off by a mask, their computation and
+ * their K/V reads skipped.
+ *   block_mask : device uint8 [mask_heads, T, T], T = ⌈N / FA_SPARSE_BLOCK⌉,
+ *             row-major; entry (r, c) nonzero keeps the scores of query rows
+ *             r·128 … r·128+127 against keys c·128 … c·128+127, zero sets them
+ *             to −∞ (like the causal mask, with which it combines when causal
+ *             is set).  T ≤ 1024 (N ≤ 131072).
+ *   mask_heads : 1 (one mask for every (b, h)) or B·H (mask of (b, h) at
+ *             index b·H + h).
+ * A query row left with no key at all gets O = 0 and L = −∞.  Other
+ * arguments, conventions and errors as for fa_fwd; FA_ERR_NULL for a NULL
+ * mask, FA_ERR_SHAPE for T > 1024 or mask_heads not in {1, B·H},
+ * FA_ERR_ALIAS when o or lse overlaps the mask. */
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int d, float scale, int causal,
+                              const unsigned char* block_mask, int mask_heads, void* stream);
 
 /* Bytes of device workspace fa_bwd needs: fp32 pairs [B, H, N, 2].
  * Returns 0 when the sizes are invalid. */

@@ -77,7 +77,7 @@ EXTRA_WORKLOADS = [
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
-_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3, "seqlens": 4, "do": 5}
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "boost": 3, "seqlens": 4, "do": 5, "mask": 6}
 
 
 def seed_for(w: Workload, tensor: str, b: int, h: int) -> int:
@@ -169,6 +169,36 @@ def make_seqlens(w: Workload) -> torch.Tensor:
     if w.B > 1:
         lens[1] = 1
     return lens.to(torch.int32)
+
+
+def make_block_mask(w: Workload, density: float, heads: int = 1, block: int = 128) -> torch.Tensor:
+    """A seeded block mask uint8 [heads, T, T], T = ⌈N/block⌉: every query block keeps
+    its own key block and key block 0 (local and global attention, so no row is
+    left empty), and each other block independently with probability ``density``."""
+    T = -(-w.N // block)
+    g = _gen(seed_for(w, "mask", 0, heads))
+    m = (torch.rand((heads, T, T), generator=g) < density).to(torch.uint8)
+    idx = torch.arange(T)
+    m[:, idx, idx] = 1
+    m[:, :, 0] = 1
+    return m
+
+
+def block_sparse_flops(w: Workload, mask: torch.Tensor, block: int = 128) -> float:
+    """4·d per (query, key) pair the mask keeps (and, when causal, the causal mask
+    keeps), summed over the heads; with one mask it is shared by every (b, h)."""
+    n = w.N
+    T = mask.shape[-1]
+    sizes = torch.tensor([min(block, n - i * block) for i in range(T)], dtype=torch.float64)
+    if w.causal:
+        # kept pairs of block (r, c): all when c < r, none when c > r, i(i+1)/2 on the diagonal
+        pairs = torch.outer(sizes, sizes)
+        pairs = torch.tril(pairs, -1) + torch.diag(sizes * (sizes + 1) / 2)
+    else:
+        pairs = torch.outer(sizes, sizes)
+    kept = (mask.to(torch.float64) * pairs).sum().item()
+    per_mask_heads = w.B * w.H / mask.shape[0]
+    return 4.0 * w.d * kept * per_mask_heads
 
 
 def prefill_flops(w: Workload) -> float:

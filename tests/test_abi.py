@@ -29,7 +29,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
-                 "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes"):
+                 "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes",
+                 "fa_fwd_block_sparse"):
         assert want in names
 
 
@@ -109,6 +110,22 @@ def test_decode_gqa_argument_checks():
     assert _gqa(wsb=need - 1) == 6
     assert _gqa(seqlens=ctypes.c_void_p(0x50000002)) == 4  # int32 lengths must be 4-byte aligned
     assert _gqa(seqlens=P[3]) == 8          # lengths inside the output
+
+
+def _bsp(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=300, d=64, scale=0.125, causal=0, mask=P[5],
+         mh=1):
+    return _lib().fa_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), causal, mask, mh, None)
+
+
+def test_block_sparse_argument_checks():
+    assert _bsp(mask=None) == 1 and _bsp(q=None) == 1
+    assert _bsp(mh=3) == 2 and _bsp(mh=0) == 2        # one mask, or one per (b, h) = 2
+    assert _bsp(N=1024 * 128 + 1) == 2                # more than 1024 key blocks
+    assert _bsp(d=80) == 3
+    assert _bsp(scale=-1.0) == 5
+    assert _bsp(o=MISALIGNED) == 4
+    assert _bsp(mask=ctypes.c_void_p(0x40000000 + 8)) == 8   # mask inside o's range
+    assert _bsp(o=P[0]) == 8
 
 
 def _bwd(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, N=16, d=64,
