@@ -55,16 +55,19 @@ def parse():
                     help="HBM traffic per launch measured with rocprofv3 --pmc (JSON), if present")
     ap.add_argument("--make-traffic", metavar="DIR",
                     help="write --traffic from rocprofv3 --pmc csv output under DIR/<COUNTER>_<kind>/ "
-                         "(COUNTER in FETCH_SIZE, WRITE_SIZE; kind in fwd, decode, copy) and exit")
+                         "(COUNTER in FETCH_SIZE, WRITE_SIZE; kind in fwd, decode, gqa, bwd, sparse, copy) and exit")
     return ap.parse_args()
 
 
 # Kernels whose HBM bytes are reported, and the sources each one is built from: a traffic
 # figure taken from an older build of those sources is stale and reported as null.
 TRAFFIC_KERNELS = {
-    "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_internal.h"]),
+    "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "decode": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
     "gqa": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
+    "bwd": (["fa_bwd_prep_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"],
+            ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]),
+    "sparse": (["fa_fwd_kernel<128, false, true>"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "copy": (["copyBuffer"], []),
 }
 
@@ -112,7 +115,7 @@ def make_traffic(args):
     f_w = gib_kib / per_launch("copy", "WRITE_SIZE")
     out = {"method": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by a 1 GiB copy",
            "fetch_scale": round(f_r, 4), "write_scale": round(f_w, 4)}
-    for kind in ("fwd", "decode", "gqa"):
+    for kind in ("fwd", "decode", "gqa", "bwd", "sparse"):
         if not os.path.isdir(os.path.join(args.make_traffic, f"FETCH_SIZE_{kind}")):
             continue
         fk, wk = per_launch(kind, "FETCH_SIZE"), per_launch(kind, "WRITE_SIZE")
@@ -225,7 +228,7 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
             "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
 
 
-def time_sparse(torch, fa, synth, dev, args):
+def time_sparse(torch, fa, synth, dev, args, traffic):
     """Block-sparse forward against the dense forward on the long workload, each timed
     W + K calls between HIP events, interleaved."""
     ws_ = synth.BY_NAME["long_noncausal_b1h16n16384d128"]
@@ -256,10 +259,11 @@ def time_sparse(torch, fa, synth, dev, args):
     return {"workload": ws_.name + "_blocksparse", "mask": "own + first key block, 10 % of the rest (seeded)",
             "kept_blocks": round(kept, 4), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(sp, 4),
             "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "dense_ms": round(dn, 4),
-            "speedup_vs_dense": round(dn / sp, 2), "ideal_speedup": round(1 / kept, 2), "algorithmic_flops": flops}
+            "speedup_vs_dense": round(dn / sp, 2), "ideal_speedup": round(1 / kept, 2), "algorithmic_flops": flops,
+            "traffic": traffic_bytes(traffic, "sparse")}
 
 
-def time_bwd(torch, fa, synth, dev, args, wf, q, k, v):
+def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
     """The backward on the prefill workload, timed on its own: the forward's O and L
     and a seeded dO, W warm-up calls, then K calls, each between HIP events."""
     print(f"[bench] backward: {wf.name}", file=sys.stderr, flush=True)
@@ -282,6 +286,8 @@ def time_bwd(torch, fa, synth, dev, args, wf, q, k, v):
     return {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(avg, 4),
             "ms_min": round(min(ms), 4), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": flops,
+            "algorithmic_bytes": float(wf.B * wf.H * (16 * wf.N * wf.d + 4 * wf.N)),
+            "traffic": traffic_bytes(traffic, "bwd"),
             "note": "three kernels per call (per-row L and D; dK, dV; dQ); the dQ pass recomputes S and dP, "
                     "so the matrix cores run 7/5 of the counted FLOPs"}
 
@@ -406,9 +412,9 @@ def main():
     if args.only in ("all", "gqa"):
         out["decode_gqa"] = time_gqa(torch, fa, synth, dev, args, traffic)
     if args.only in ("all", "bwd"):
-        out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v)
+        out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic)
     if args.only in ("all", "sparse"):
-        out["block_sparse"] = time_sparse(torch, fa, synth, dev, args)
+        out["block_sparse"] = time_sparse(torch, fa, synth, dev, args, traffic)
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)
