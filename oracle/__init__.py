@@ -26,6 +26,7 @@ from .ref import (
     attention_ref,
     decode_ref,
     decode_gqa_ref,
+    decode_paged_ref,
     attention_bwd_ref,
     attention_block_sparse_ref,
 )
@@ -37,6 +38,7 @@ __all__ = [
     "attention_ref",
     "decode_ref",
     "decode_gqa_ref",
+    "decode_paged_ref",
     "attention_bwd_ref",
     "attention_block_sparse_ref",
     "bf16_half_ulp",

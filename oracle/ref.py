@@ -160,6 +160,34 @@ def decode_gqa_ref(q, k, v, scale, seqlens=None):
     return o, lse
 
 
+def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale):
+    """Grouped-query decode over a paged K/V cache.
+
+    k_pages, v_pages: [num_pages, Hkv, P, d] — page p of K/V head h holds P
+    consecutive keys; block_table: [B, max_pages] page numbers; key t of
+    sequence b sits at row t mod P of page block_table[b, ⌊t/P⌋].  Paging is a
+    storage layout of the cache (the pages set it beside tiled computation:
+    [FA-1拆解], closing section, on paged K/V caches), so the result is that
+    of ``decode_gqa_ref`` on the keys gathered in order: the gather is written
+    out here and the definition reused.  Returns (O [B, Hq, d], LSE [B, Hq]).
+    """
+    k_pages = as_f64(k_pages)
+    v_pages = as_f64(v_pages)
+    table = np.asarray(block_table)
+    lens = [int(x) for x in np.asarray(seqlens)]
+    B = table.shape[0]
+    _, Hkv, P, d = k_pages.shape
+    Lmax = table.shape[1] * P
+    k = np.zeros((B, Hkv, Lmax, d))
+    v = np.zeros((B, Hkv, Lmax, d))
+    for b in range(B):
+        for t in range(lens[b]):
+            page = int(table[b, t // P])
+            k[b, :, t] = k_pages[page, :, t % P]
+            v[b, :, t] = v_pages[page, :, t % P]
+    return decode_gqa_ref(q, k, v, scale, seqlens=lens)
+
+
 def attention_block_sparse_ref(q, k, v, scale, causal, block_mask, block=128, rows=None):
     """Block-sparse attention ([FA-1拆解] "块稀疏扩展"): standard attention in which
     every score whose (query block, key block) is switched off in the block

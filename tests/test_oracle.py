@@ -17,8 +17,8 @@ import numpy as np
 import pytest
 import scipy.special
 
-from oracle import (attention_block_sparse_ref, attention_bwd_ref, attention_ref, decode_gqa_ref, decode_ref,
-                    safe_softmax, scores)
+from oracle import (attention_block_sparse_ref, attention_bwd_ref, attention_ref, decode_gqa_ref, decode_paged_ref,
+                    decode_ref, safe_softmax, scores)
 from oracle.compare import bf16_half_ulp, bf16_rne, bwd_allowance, check_bwd, check_prefill
 import _method_fp64 as M
 
@@ -476,6 +476,43 @@ def test_bf16_rounding_helpers():
     assert r["pass"] and r["floor"] > 0
     r = check_prefill(x + 0.02, [0.0], x, [0.0])
     assert not r["ok"]
+
+
+# --------------------------------------------------------------------------
+# paged K/V decode
+
+
+def test_decode_paged_is_the_contiguous_cache_scattered_into_pages():
+    """Scatter a contiguous cache into pages under a random page permutation: the
+    paged decode must see the same keys in the same order (checked against
+    decode_ref head by head, which the gather does not use)."""
+    rng = np.random.default_rng(81)
+    B, Hq, Hkv, P, d, max_pages = 3, 4, 2, 8, 16, 5
+    Lmax = P * max_pages
+    k = rng.standard_normal((B, Hkv, Lmax, d))
+    v = rng.standard_normal((B, Hkv, Lmax, d))
+    q = rng.standard_normal((B, Hq, d))
+    n_pages = B * max_pages + 3
+    perm = rng.permutation(n_pages)[: B * max_pages].reshape(B, max_pages)
+    kp = rng.standard_normal((n_pages, Hkv, P, d))   # pages nobody maps hold noise
+    vp = rng.standard_normal((n_pages, Hkv, P, d))
+    for b in range(B):
+        for i in range(max_pages):
+            kp[perm[b, i]] = k[b, :, i * P:(i + 1) * P]
+            vp[perm[b, i]] = v[b, :, i * P:(i + 1) * P]
+    lens = np.array([Lmax, 1, 29])
+    o, l = decode_paged_ref(q, kp, vp, perm, lens, 0.3)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            ro, rl = decode_ref(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1, :lens[b]], v[b:b + 1, kh:kh + 1, :lens[b]], 0.3)
+            np.testing.assert_allclose(o[b, h], ro[0, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l[b, h], rl[0, 0], rtol=0, atol=1e-13)
+    # a page past a sequence's length is never read: poisoning it changes nothing
+    kp2 = kp.copy()
+    kp2[perm[1, 1]] = np.nan
+    o2, _ = decode_paged_ref(q, kp2, vp, perm, lens, 0.3)
+    np.testing.assert_array_equal(o2[1], o[1])
 
 
 # --------------------------------------------------------------------------
