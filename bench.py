@@ -17,6 +17,8 @@ Each call is also timed with HIP events recorded on the stream it runs on
                      block mask (own and first key block, 10 % of the rest),
                      against fa_fwd on the same inputs: TFLOP/s of the kept
                      blocks and the speed-up over the dense call
+  * decode_paged     the same grouped-query decode over the cache laid out in
+                     64-key pages in a seeded random order (fa_decode_paged)
   * backward         fa_bwd on the prefill workload (the step's O and L, a
                      seeded dO), timed on its own after the step: TFLOP/s of
                      the five N×N×d products, 10·N²·d·B·H / 2 (causal)
@@ -221,11 +223,29 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
     avg = sum(ms) / len(ms)
     gbytes = synth.decode_bytes(wg)
     gbs = gbytes / (avg * 1e-3) / 1e9
+    res = {"workload": wg.name, "B": wg.B, "Hq": wg.H, "Hkv": wg.kv_heads, "Lkv": wg.lkv, "d": wg.d,
+           "num_splits": wg.num_splits, "value": round(gbs, 1), "unit": "GB/s", "ms": round(avg, 4),
+           "ms_min": round(min(ms), 4), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
+    # the same cache in 64-key pages under a seeded random page order
+    kp, vp, tbl = synth.paginate(kg, vg, 64, seed=5)
     del kg, vg
-    return {"workload": wg.name, "B": wg.B, "Hq": wg.H, "Hkv": wg.kv_heads, "Lkv": wg.lkv, "d": wg.d,
-            "num_splits": wg.num_splits, "value": round(gbs, 1), "unit": "GB/s", "ms": round(avg, 4),
-            "ms_min": round(min(ms), 4), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": gbytes, "traffic": traffic_bytes(traffic, "gqa")}
+    for _ in range(args.warmup):
+        fa.fa_decode_paged(qg, kp, vp, tbl, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record()
+        fa.fa_decode_paged(qg, kp, vp, tbl, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    pavg = sum(ms) / len(ms)
+    pgbs = gbytes / (pavg * 1e-3) / 1e9
+    del kp, vp
+    paged = {"workload": wg.name + "_paged64", "page_size": 64, "value": round(pgbs, 1), "unit": "GB/s",
+             "ms": round(pavg, 4), "ms_min": round(min(ms), 4), "frac_hbm_peak": round(pgbs / HBM_PEAK_GBS, 4),
+             "vs_contiguous": round(avg / pavg, 3)}
+    return res, paged
 
 
 def time_sparse(torch, fa, synth, dev, args, traffic):
@@ -410,7 +430,7 @@ def main():
                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_bytes(traffic, "decode"), "algorithmic_bytes": dbytes}
     if args.only in ("all", "gqa"):
-        out["decode_gqa"] = time_gqa(torch, fa, synth, dev, args, traffic)
+        out["decode_gqa"], out["decode_paged"] = time_gqa(torch, fa, synth, dev, args, traffic)
     if args.only in ("all", "bwd"):
         out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic)
     if args.only in ("all", "sparse"):

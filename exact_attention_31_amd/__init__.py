@@ -9,6 +9,7 @@ library is missing or fails to load, the calls raise.
     fa_fwd(q, k, v, scale=None, causal=False)        -> (o, lse)
     fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
     fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None) -> (o, lse)
+    fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, ...) -> (o, lse)
     fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
     fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False) -> (o, lse)
     fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
@@ -63,6 +64,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, f, i, vp, sz, vp]
+    lib.fa_decode_paged.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_fwd_tile_pairs.argtypes = [i, i, i]
@@ -317,3 +320,53 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, scale=None, num_splits=None, workspace=None):
+    """Grouped-query split-KV decode over a paged cache: q bf16 [B, Hq, 1, d];
+    k_pages/v_pages bf16 [num_pages, Hkv, page_size, d]; block_table int32
+    [B, max_pages] (device); seqlens int32 [B] (device) or None (all
+    max_pages·page_size keys).  Returns (o bf16 [B, Hq, 1, d], lse fp32 [B, Hq])."""
+    torch = _torch()
+    _check(q, "q", 4)
+    _check(k_pages, "k_pages", 4)
+    _check(v_pages, "v_pages", 4)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence, q has {one}")
+    if k_pages.shape != v_pages.shape or k_pages.shape[3] != d:
+        raise ValueError("k_pages/v_pages shapes must match and end in d")
+    num_pages, Hkv, page_size = k_pages.shape[:3]
+    if Hq % Hkv:
+        raise ValueError(f"query heads {Hq} are not a multiple of K/V heads {Hkv}")
+    t = block_table
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] != B:
+        raise TypeError("block_table must be an int32 tensor [B, max_pages]")
+    if t.device != q.device or not t.is_contiguous():
+        raise ValueError("block_table must be contiguous and on q's device")
+    max_pages = t.shape[1]
+    sl = None
+    if seqlens is not None:
+        if not isinstance(seqlens, torch.Tensor) or seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+            raise TypeError("seqlens must be an int32 tensor of shape [B]")
+        if seqlens.device != q.device or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be contiguous and on q's device")
+        sl = seqlens.data_ptr()
+    L = max_pages * page_size
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        g = Hq // Hkv
+        num_splits = default_splits(B * Hkv * (g // _group_width(g)), L)
+    need = fa_decode_workspace_bytes(B, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = load_library().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), B, Hq, Hkv, d, page_size, num_pages, t.data_ptr(), max_pages,
+                                        sl, float(scale), int(num_splits), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_paged")
+    return o, lse

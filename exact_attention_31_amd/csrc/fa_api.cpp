@@ -197,20 +197,29 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return o_bytes + parts * 4;
 }
 
-fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                        int Lmax, int d, const int* seqlens, float scale, int num_splits, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Split-KV decode, contiguous (block_table == nullptr: K/V [B, Hkv, Lmax, d])
+// or paged (K/V pools [num_pages, Hkv, 2^page_shift, d], Lmax = max_pages << page_shift).
+fa_status decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Lmax, int d, const int* seqlens, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, const int* block_table, int max_pages, int page_shift, int num_pages,
+                      void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const size_t kv_elems = count4(B, Hkv, Lmax, d);
+  // bytes of K (and of V): the (b, head) caches, or the page pool
+  const size_t kv_elems = block_table ? count4(num_pages, Hkv, 1 << page_shift, d) : count4(B, Hkv, Lmax, d);
   if (kv_elems == 0 || count4(B, Hq, 1, d) == 0 || (unsigned long long)B * Hq * num_splits > 0x7fffffffull)
     return FA_ERR_SHAPE;
+  if (block_table && (unsigned long long)num_pages * Hkv << page_shift > 0x7fffffffull) return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f) || num_splits < 1 || num_splits > Lmax) return FA_ERR_VALUE;
   const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
     return FA_ERR_ALIGN;
   const size_t qb = (size_t)B * Hq * d * 2, kb = kv_elems * 2, lb = (size_t)B * Hq * 4;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) || overlap(lse, lb, q, qb) ||
@@ -221,6 +230,11 @@ fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, fl
   if (seqlens) {
     const size_t sb = (size_t)B * 4;
     if (overlap(o, qb, seqlens, sb) || overlap(lse, lb, seqlens, sb) || overlap(workspace, need, seqlens, sb))
+      return FA_ERR_ALIAS;
+  }
+  if (block_table) {
+    const size_t tb = (size_t)B * max_pages * 4;
+    if (overlap(o, qb, block_table, tb) || overlap(lse, lb, block_table, tb) || overlap(workspace, need, block_table, tb))
       return FA_ERR_ALIAS;
   }
 
@@ -240,8 +254,37 @@ fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, fl
   p.S = num_splits;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_shift = page_shift;
+  p.num_pages = num_pages;
   if (fa::launch_decode(p, B, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                        int Lmax, int d, const int* seqlens, float scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Lmax, d, seqlens, scale, num_splits, workspace, workspace_bytes,
+                     nullptr, 0, 0, 0, stream);
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse, int B, int Hq,
+                          int Hkv, int d, int page_size, int num_pages, const int* block_table, int max_pages,
+                          const int* seqlens, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!block_table) return FA_ERR_NULL;
+  if (num_pages < 1 || max_pages < 1 || page_size < 1 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
+    return FA_ERR_SHAPE;
+  if ((unsigned long long)max_pages * page_size > 0x7fffffffull) return FA_ERR_SHAPE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  return decode_impl(q, k_pages, v_pages, o, lse, B, Hq, Hkv, max_pages * page_size, d, seqlens, scale, num_splits,
+                     workspace, workspace_bytes, block_table, max_pages, shift, num_pages, stream);
 }
 
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lkv,

@@ -81,7 +81,14 @@ __device__ inline uint16_t to_bf16(float x) {
 // summary carries weight exactly 0 after the merge.
 __device__ inline float safe_mc(float m, float c) { return m == -INFINITY ? 0.f : m * c; }
 
-template <int D, int GQ>
+// Paged K/V (PAGED): the cache is a pool of pages, page × K/V head holding
+// 2^page_shift consecutive keys; a sequence's keys follow its row of the block
+// table.  The workgroup copies the page numbers of its segment into LDS
+// (clamped into the pool) in chunks of kPageChunk and maps each key to its row
+// through them; the streaming and the arithmetic are unchanged.
+constexpr int kPageChunk = 1024;
+
+template <int D, int GQ, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPI = 64 / LPK;     // keys per wavefront instruction
@@ -120,8 +127,9 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodePara
 #pragma unroll
     for (int e = 0; e < 4; ++e) qw[i][e] = w[e];
   }
-  const uint16_t* __restrict__ kb = p.k + (size_t)bk * p.L * D + chunk * 8;
-  const uint16_t* __restrict__ vb = p.v + (size_t)bk * p.L * D + chunk * 8;
+  // row r of the (b, K/V head) cache, or of the page pool when PAGED
+  const uint16_t* __restrict__ kb = p.k + (PAGED ? 0 : (size_t)bk * p.L * D) + chunk * 8;
+  const uint16_t* __restrict__ vb = p.v + (PAGED ? 0 : (size_t)bk * p.L * D) + chunk * 8;
 
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
@@ -132,17 +140,26 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodePara
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   }
 
-  for (int k0 = k_begin; k0 < k_end; k0 += UNR * STEP) {
+  __shared__ int page_row[PAGED ? kPageChunk : 1];  // first pool row of each page of the chunk
+  const int hk = bk % p.Hkv;
+  // keys [c_begin, c_end) of the segment; PAGED: pages from page0 on are in page_row
+  auto run = [&](int c_begin, int c_end, int page0) __attribute__((always_inline)) {
+  for (int k0 = c_begin; k0 < c_end; k0 += UNR * STEP) {
     u32x4_t kr[UNR], vr[UNR];
     int key[UNR];
+    size_t row[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       key[u] = k0 + (u * kDecWaves + wave) * KPI + slot;
-      kr[u] = key[u] < k_end ? *reinterpret_cast<const u32x4_t*>(kb + (size_t)key[u] * D) : u32x4_t{0, 0, 0, 0};
+      if (PAGED)
+        row[u] = key[u] < c_end ? (size_t)page_row[(key[u] >> p.page_shift) - page0] + (key[u] & ((1 << p.page_shift) - 1)) : 0;
+      else
+        row[u] = (size_t)key[u];
+      kr[u] = key[u] < c_end ? *reinterpret_cast<const u32x4_t*>(kb + row[u] * D) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      vr[u] = key[u] < k_end ? *reinterpret_cast<const u32x4_t*>(vb + (size_t)key[u] * D) : u32x4_t{0, 0, 0, 0};
+      vr[u] = key[u] < c_end ? *reinterpret_cast<const u32x4_t*>(vb + row[u] * D) : u32x4_t{0, 0, 0, 0};
 
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodePara
           t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[i][e]),
                                               __builtin_bit_cast(bf16x2_t, (uint32_t)kr[u][e]), t, false);
         t = row_sum<LPK>(t);
-        sc[u] = key[u] < k_end ? t : -INFINITY;
+        sc[u] = key[u] < c_end ? t : -INFINITY;
         bm = fmaxf(bm, sc[u]);
       }
       const float m_new = fmaxf(m[i], bm);
@@ -176,6 +193,25 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecodePara
         }
       }
       m[i] = m_new;
+    }
+  }
+  };
+  if (!PAGED) {
+    run(k_begin, k_end, 0);
+  } else if (k_end > k_begin) {
+    const int sh = p.page_shift;
+    const int first_page = k_begin >> sh, last_page = (k_end - 1) >> sh;
+    const int* tbl = p.block_table + (size_t)b * p.max_pages;
+    for (int pc = first_page; pc <= last_page; pc += kPageChunk) {
+      const int np = min(kPageChunk, last_page - pc + 1);
+      __syncthreads();  // the previous chunk's rows are no longer read
+      for (int i = tid; i < np; i += kDecThreads) {
+        int pg = tbl[pc + i];
+        pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+        page_row[i] = (pg * p.Hkv + hk) << sh;
+      }
+      __syncthreads();
+      run(max(k_begin, pc << sh), min(k_end, (pc + np) << sh), pc);
     }
   }
 
@@ -298,7 +334,10 @@ __global__ __launch_bounds__(kCombThreads) void fa_decode_combine_kernel(DecodeP
 template <int D, int GQ>
 hipError_t launch_decode_t(const DecodeParams& p, int B, hipStream_t stream) {
   const long long groups = (long long)B * p.Hkv * (p.G / GQ);
-  hipLaunchKernelGGL((fa_decode_split_kernel<D, GQ>), dim3((unsigned)(groups * p.S)), dim3(kDecThreads), 0, stream, p);
+  if (p.block_table)
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, GQ, true>), dim3((unsigned)(groups * p.S)), dim3(kDecThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, GQ, false>), dim3((unsigned)(groups * p.S)), dim3(kDecThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fa_decode_combine_kernel<D>, dim3(B * p.Hq), dim3(kCombThreads), 0, stream, p);

@@ -66,6 +66,10 @@ struct DecodeParams {
   int S;
   float scale;
   float scale_log2;
+  const int* block_table;  // null: K/V contiguous per (b, K/V head); else [B, max_pages] page numbers
+  int max_pages;     // entries per block-table row
+  int page_shift;    // keys per page = 2^page_shift
+  int num_pages;     // pages in the pool (entries are clamped into it)
 };
 
 struct BwdParams {

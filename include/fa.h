@@ -16,7 +16,8 @@
  *              the keys split into segments whose partial results are merged by
  *              the ⊕ log-sum-exp combine ([15-779 L5] §8.4, §4.4–4.5);
  *              fa_decode_gqa adds grouped query heads (several query heads per
- *              cached K/V head) and per-sequence key counts.
+ *              cached K/V head) and per-sequence key counts, fa_decode_paged
+ *              reads the cache through a page table.
  *   fa_fwd_block_sparse  fa_fwd with blocks of the score matrix switched off
  *              by a block mask, their work and K/V traffic skipped
  *              ([FA-1拆解] "块稀疏扩展").
@@ -177,6 +178,29 @@ fa_status fa_decode_gqa(const void* q, const void* k, const void* v, void* o, fl
                         int B, int Hq, int Hkv, int Lmax, int d, const int* seqlens,
                         float scale, int num_splits, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Grouped-query split-KV decode over a paged K/V cache.
+ *   k_pages, v_pages : bf16 [num_pages, Hkv, page_size, d] — a pool of pages;
+ *             page p of K/V head h holds page_size consecutive keys of one
+ *             sequence, contiguous (page_size·d elements).
+ *   block_table : device int32 [B, max_pages] (4-byte aligned): key t of
+ *             sequence b is row t mod page_size of page
+ *             block_table[b·max_pages + ⌊t/page_size⌋].  Entries outside
+ *             [0, num_pages) are clamped into it (the device reads them).
+ *   page_size : a power of two, 1 … 4096.
+ *   seqlens : as for fa_decode_gqa, with Lmax = max_pages·page_size; NULL:
+ *             every sequence holds Lmax keys.
+ * The result is fa_decode_gqa's on the cache the table describes (the same
+ * keys in the same order, the same arithmetic).  Paging is a layout of the
+ * cache, which the pages set beside tiled computation ([FA-1拆解], closing
+ * section).  Other arguments, workspace and errors as for fa_decode_gqa;
+ * FA_ERR_NULL for a NULL table, FA_ERR_SHAPE for a page size that is not a
+ * power of two in range, num_pages or max_pages < 1, or a pool of 2^31 rows
+ * or more. */
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                          int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                          const int* block_table, int max_pages, const int* seqlens, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
  * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not

@@ -159,6 +159,23 @@ def make_decode_kv(w: Workload, device="cpu"):
     return k, v
 
 
+def paginate(k: torch.Tensor, v: torch.Tensor, page_size: int, seed: int):
+    """The cache k, v [B, Hkv, L, d] (L a multiple of page_size) laid out as a pool of
+    pages [B·L/page_size, Hkv, page_size, d] in a seeded random order, with the block
+    table int32 [B, L/page_size] that maps each sequence's page i to its pool page
+    (all on k's device)."""
+    B, Hkv, L, d = k.shape
+    n = L // page_size
+    perm = torch.randperm(B * n, generator=_gen(seed)).to(torch.int32)
+    pools = []
+    for x in (k, v):
+        pages = x.reshape(B, Hkv, n, page_size, d).permute(0, 2, 1, 3, 4).reshape(B * n, Hkv, page_size, d)
+        pool = torch.empty_like(pages)
+        pool[perm.to(torch.int64).to(x.device)] = pages
+        pools.append(pool)
+    return pools[0], pools[1], perm.reshape(B, n).to(k.device)
+
+
 def make_seqlens(w: Workload) -> torch.Tensor:
     """Per-sequence key counts for a ragged decode batch: int32 [B], uniform on
     [1, Lkv] from a seeded generator, with the first sequence at the full Lkv

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
                  "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes",
-                 "fa_fwd_block_sparse"):
+                 "fa_fwd_block_sparse", "fa_decode_paged"):
         assert want in names
 
 
@@ -149,6 +149,25 @@ def test_bwd_argument_checks():
     assert _bwd(dk=P[6]) == 8                               # two outputs on one buffer
     assert _bwd(ws=ctypes.c_void_p(0x50000000 + 16)) == 8   # workspace inside dO's range
     assert _lib().fa_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def _paged(q=P[0], kp=P[1], vp=P[2], o=P[3], lse=P[4], B=2, Hq=4, Hkv=2, d=64, ps=16, npg=8, tbl=P[5], mp=4,
+           seqlens=None, scale=0.125, S=4, ws=P[6], wsb=1 << 20):
+    return _lib().fa_decode_paged(q, kp, vp, o, lse, B, Hq, Hkv, d, ps, npg, tbl, mp, seqlens, ctypes.c_float(scale), S,
+                                  ws, wsb, None)
+
+
+def test_decode_paged_argument_checks():
+    assert _paged(tbl=None) == 1 and _paged(kp=None) == 1
+    assert _paged(ps=24) == 2 and _paged(ps=0) == 2 and _paged(ps=8192) == 2   # powers of two up to 4096
+    assert _paged(npg=0) == 2 and _paged(mp=0) == 2
+    assert _paged(npg=1 << 20, Hkv=2, Hq=4, ps=4096) == 2                      # pool of 2^33 rows
+    assert _paged(d=80) == 3
+    assert _paged(S=65) == 5                                                   # more splits than 4·16 keys
+    assert _paged(ws=None) == 6
+    assert _paged(tbl=ctypes.c_void_p(0x60000002)) == 4                        # int32 table, 4-byte aligned
+    assert _paged(tbl=P[3]) == 8                                               # table inside the output
+    assert _paged(o=P[1]) == 8                                                 # output inside the K pool
 
 
 def test_tile_shape():
