@@ -522,12 +522,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   const float c = p.scale_log2;
   const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;  // last key this row sees
 
-  auto step = [&](int j, auto buf) __attribute__((always_inline)) {
+  // CLEAN: every row of the workgroup sees every key of the tile (no mask, no skip)
+  auto step = [&](int j, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
+    constexpr bool CLEAN = decltype(clean)::value;
     const int kv0 = j * BN;
-    if (CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
+    if (!CLEAN && CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
     const unsigned char* kb = kbufs[B];
     const unsigned char* vb = vbufs[B];
+    // lane offsets opaque here: addresses are formed as offset + constant
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) asm volatile("" : "+v"(rd.row[kk]));
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(rd.tr0[ds]), "+v"(rd.tr8[ds]));
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) s[sub] = dp[sub] = f32x16_t{};
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(kb, kk, sub), qf[kk], s[sub], 0, 0, 0);
         dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(vb, kk, sub), of[kk], dp[sub], 0, 0, 0);
       }
-    const bool edge = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > wq0);
+    const bool edge = !CLEAN && ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > wq0));
     float dsr[32];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -567,17 +574,27 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   for (int kk = 0; kk < T::KS; ++kk)
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[kk])), "v"(__builtin_bit_cast(u32x4_t, of[kk])));
   asm volatile("" ::"v"(ld.x), "v"(ld.y));
-  auto body = [&](int j, auto buf) __attribute__((always_inline)) {
+  auto body = [&](int j, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     wait_stage(j + 1 < n_tiles);
     block_barrier();
     if (j + 2 < n_tiles) issue(j + 2, std::integral_constant<int, (B + 2) % 3>{});
-    step(j, buf);
+    step(j, buf, clean);
   };
-  for (int j = 0; j < n_tiles; j += 3) {
-    body(j, I0{});
-    if (j + 1 < n_tiles) body(j + 1, I1{});
-    if (j + 2 < n_tiles) body(j + 2, I2{});
+  using Y = std::true_type;
+  using G = std::false_type;
+  // tiles 0 .. n_clean-1 are whole and before the diagonal of every row of the block
+  const int n_clean = CAUSAL ? min(N / BN, (q0 + 1) / BN) : N / BN;
+  int j = 0;
+  for (; j + 3 <= n_clean; j += 3) {
+    body(j, I0{}, Y{});
+    body(j + 1, I1{}, Y{});
+    body(j + 2, I2{}, Y{});
+  }
+  for (; j < n_tiles; j += 3) {
+    body(j, I0{}, G{});
+    if (j + 1 < n_tiles) body(j + 1, I1{}, G{});
+    if (j + 2 < n_tiles) body(j + 2, I2{}, G{});
   }
 
   if (q_row < N) {
