@@ -538,29 +538,67 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) s[sub] = dp[sub] = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < T::KS; ++kk)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(kb, kk, sub), qf[kk], s[sub], 0, 0, 0);
-        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.rows(vb, kk, sub), of[kk], dp[sub], 0, 0, 0);
-      }
     const bool edge = !CLEAN && ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > wq0));
-    float dsr[32];
+    // A: S, dP of key sub-tile 0; B: those of sub-tile 1 with the vector work of
+    // sub-tile 0; C: dQ of sub-tile 0's keys with that of sub-tile 1; D: the rest
+    constexpr int NA = 2 * T::KS;      // MFMAs of S and dP per 32-key sub-tile
+    constexpr int NC = 2 * T::DSUB;    // dQ MFMAs per 32 keys (two k-steps)
+    constexpr int LA = 4, LC = 2;
+    auto op_a = [&](int j2) __attribute__((always_inline)) {  // j2: sub-tile j2 / NA, k-step (j2 % NA) / 2, K or V
+      return rd.rows((j2 & 1) ? vb : kb, (j2 % NA) >> 1, j2 / NA);
+    };
+    auto mfma_a = [&](int j2, bf16x8_t a) __attribute__((always_inline)) {
+      const int sub = j2 / NA, kk = (j2 % NA) >> 1;
+      if (j2 & 1)
+        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[kk], dp[sub], 0, 0, 0);
+      else
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[sub], 0, 0, 0);
+    };
+    u32x4_t sw[4];
+    float dsr2[2];
+    auto soft_el = [&](int sub, int r) __attribute__((always_inline)) {
+      float e = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -ld.x));
+      if (edge && kv0 + sub * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > lim) e = 0.f;
+      dsr2[r & 1] = e * (dp[sub][r] - ld.y);
+      if (r & 1) sw[2 * sub + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsr2[0], dsr2[1]);
+    };
+    auto op_c = [&](int m) __attribute__((always_inline)) {  // m: k-step m / DSUB, d sub-tile m % DSUB
+      return rd.tr(kb, m % T::DSUB, m / T::DSUB);
+    };
+    auto mfma_c = [&](int m, bf16x8_t a) __attribute__((always_inline)) {
+      dq[m % T::DSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, sw[m / T::DSUB]),
+                                                              dq[m % T::DSUB], 0, 0, 0);
+    };
+    bf16x8_t ra[LA], rc[LC];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int t = 0; t < LA; ++t) ra[t] = op_a(t);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -ld.x));
-        if (edge && kv0 + sub * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > lim) e = 0.f;
-        dsr[16 * sub + r] = e * (dp[sub][r] - ld.y);
+    for (int t = 0; t < NA; ++t) {  // A
+      mfma_a(t, ra[t % LA]);
+      ra[t % LA] = op_a(t + LA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = NA; t < 2 * NA; ++t) {  // B
+      mfma_a(t, ra[t % LA]);
+      if (t + LA < 2 * NA)
+        ra[t % LA] = op_a(t + LA);
+      else if (t + LA - 2 * NA < LC)
+        rc[t + LA - 2 * NA] = op_c(t + LA - 2 * NA);
+#pragma unroll
+      for (int r = (t - NA) * (16 / NA); r < (t - NA + 1) * (16 / NA); ++r) soft_el(0, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < 2 * NC; ++m) {  // C and D
+      mfma_c(m, rc[m % LC]);
+      if (m + LC < 2 * NC) rc[m % LC] = op_c(m + LC);
+      if (m < NC) {
+#pragma unroll
+        for (int r = m * (16 / NC); r < (m + 1) * (16 / NC); ++r) soft_el(1, r);
       }
-#pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      const bf16x8_t sb = pack8(dsr + 8 * kk);
-#pragma unroll
-      for (int ds = 0; ds < T::DSUB; ++ds)
-        dq[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(kb, ds, kk), sb, dq[ds], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
