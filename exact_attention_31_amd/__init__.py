@@ -14,6 +14,8 @@ library is missing or fails to load, the calls raise.
     fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False) -> (o, lse)
     fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, N)                  -> int
+    fa_bwd_atomic(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+    fa_bwd_atomic_workspace_bytes(B, H, N, d)        -> int
     fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
     fa_fwd_tile_shape(d)                             -> (block_m, block_n)
     fa_status_str(status)                            -> str
@@ -64,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_atomic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_atomic.restype = i
+    lib.fa_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_atomic_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, f, i, vp, sz, vp]
     lib.fa_decode_paged.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -106,6 +112,10 @@ def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def fa_bwd_atomic_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_atomic_workspace_bytes(int(B), int(H), int(N), int(d)))
 
 
 def _torch():
@@ -288,14 +298,7 @@ def fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None, workspace=
     return o, lse
 
 
-def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
-    """Backward of fa_fwd: q, k, v, o, do bf16 [B, H, N, d], lse fp32 [B, H, N]
-    (o and lse as fa_fwd returned them, do the gradient with respect to o).
-
-    Returns (dq, dk, dv), bf16 [B, H, N, d].  ``scale`` and ``causal`` must be
-    the forward's.  The workspace (fa_bwd_workspace_bytes) is allocated with
-    torch when not given.  Runs on the current stream.
-    """
+def _bwd_call(fn, q, k, v, o, lse, do, scale, causal, workspace):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check(t, n, 4)
@@ -309,17 +312,35 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = fa_bwd_workspace_bytes(B, H, N)
+    need = fa_bwd_atomic_workspace_bytes(B, H, N, d) if fn == "fa_bwd_atomic" else fa_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                               float(scale), int(bool(causal)), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    st = getattr(load_library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                                     float(scale), int(bool(causal)), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, fn)
     return dq, dk, dv
+
+
+def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
+    """Backward of fa_fwd: q, k, v, o, do bf16 [B, H, N, d], lse fp32 [B, H, N]
+    (o and lse as fa_fwd returned them, do the gradient with respect to o).
+
+    Returns (dq, dk, dv), bf16 [B, H, N, d].  ``scale`` and ``causal`` must be
+    the forward's.  The workspace (fa_bwd_workspace_bytes) is allocated with
+    torch when not given.  Runs on the current stream.  Deterministic.
+    """
+    return _bwd_call("fa_bwd", q, k, v, o, lse, do, scale, causal, workspace)
+
+
+def fa_bwd_atomic(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
+    """fa_bwd in one key-block pass, dQ added up with atomics: same arguments and
+    results up to the order of dQ's fp32 additions (not bit-reproducible).  The
+    workspace is fa_bwd_atomic_workspace_bytes(B, H, N, d) bytes."""
+    return _bwd_call("fa_bwd_atomic", q, k, v, o, lse, do, scale, causal, workspace)
 
 
 def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, scale=None, num_splits=None, workspace=None):

@@ -138,9 +138,16 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)rows * 8;
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The dQ accumulator starts on the next 256-byte boundary after the (L, D) pairs.
+size_t dqacc_offset(size_t ld_bytes) { return (ld_bytes + 255) & ~(size_t)255; }
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                   size_t workspace_bytes, bool fused, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -149,7 +156,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
       (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
     return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  const size_t need = fused ? fa_bwd_atomic_workspace_bytes(B, H, N, d) : fa_bwd_workspace_bytes(B, H, N);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
@@ -177,6 +184,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.ld = static_cast<float*>(workspace);
+  p.dqacc = fused ? reinterpret_cast<float*>(static_cast<char*>(workspace) + dqacc_offset(fa_bwd_workspace_bytes(B, H, N)))
+                  : nullptr;
   p.BH = B * H;
   p.N = N;
   p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
@@ -188,6 +197,30 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.scale_log2 = scale * kLog2e;
   if (fa::launch_bwd(p, d, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_atomic_workspace_bytes(int B, int H, int N, int d) {
+  const size_t ld = fa_bwd_workspace_bytes(B, H, N);
+  if (ld == 0 || (d != 64 && d != 128)) return 0;
+  return dqacc_offset(ld) + (size_t)B * H * N * d * 4;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes, false,
+                  stream);
+}
+
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes, true,
+                  stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {

@@ -91,24 +91,31 @@ struct TileReads {
   int row[T::KS];    // 16-byte row reads: row i32 (+32 per sub-tile), chunk 2kk + g
   int tr0[T::DSUB];  // transpose reads, rows 4g + jj/4 (+16 per k-step)
   int tr8[T::DSUB];  // the same 8 rows further on (the swizzle has period 16)
+  // offsets of the transpose reads of d sub-tile ds (rows 4g + jj/4 and 8 on)
+  __device__ static int tr_off(int lane, int ds, int plus8) {
+    const int jj = lane & 15;
+    const int r = 4 * (lane >> 5) + (jj >> 2) + 8 * plus8;
+    const int cl = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+    return r * T::ROW + (((4 * ds + cl) ^ T::swz(r)) << 4) + 8 * (jj & 1);
+  }
   __device__ void init(int lane) {
-    const int i32 = lane & 31, g = lane >> 5, jj = lane & 15;
+    const int i32 = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < T::KS; ++kk) row[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::swz(i32)) << 4);
-    const int r = 4 * g + (jj >> 2);
-    const int cl = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds) {
-      tr0[ds] = r * T::ROW + (((4 * ds + cl) ^ T::swz(r)) << 4) + 8 * (jj & 1);
-      tr8[ds] = (r + 8) * T::ROW + (((4 * ds + cl) ^ T::swz(r + 8)) << 4) + 8 * (jj & 1);
+      tr0[ds] = tr_off(lane, ds, 0);
+      tr8[ds] = tr_off(lane, ds, 1);
     }
   }
-  // A operand of one k-step (16 rows) of a product whose reduction index is the row.
-  __device__ bf16x8_t tr(const unsigned char* b, int ds, int kk) const {
-    const u32x2_t a0 = lds_tr_read(b, tr0[ds] + 16 * kk * T::ROW);
-    const u32x2_t a1 = lds_tr_read(b, tr8[ds] + 16 * kk * T::ROW);
+  // A operand of one k-step (16 rows) of a product whose reduction index is the row,
+  // from the offsets of its two halves.
+  __device__ static bf16x8_t tr_at(const unsigned char* b, int o0, int o8, int kk) {
+    const u32x2_t a0 = lds_tr_read(b, o0 + 16 * kk * T::ROW);
+    const u32x2_t a1 = lds_tr_read(b, o8 + 16 * kk * T::ROW);
     return __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
   }
+  __device__ bf16x8_t tr(const unsigned char* b, int ds, int kk) const { return tr_at(b, tr0[ds], tr8[ds], kk); }
   // A operand of one k-step (16 of d) for the 32 rows of sub-tile `sub`.
   __device__ bf16x8_t rows(const unsigned char* b, int kk, int sub) const {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(b + row[kk] + sub * 32 * T::ROW));
@@ -156,6 +163,26 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
   for (int w = CH / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, CH);
   if (row < rows_total && c == 0)
     reinterpret_cast<float2*>(p.ld)[row] = make_float2(p.lse[row] * 1.4426950408889634f, acc);
+  if (p.dqacc && row < rows_total) {  // the fused backward's dQ accumulator starts at zero
+    float4* z = reinterpret_cast<float4*>(p.dqacc + (size_t)row * D + 8 * c);
+    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// dQ = scale · the fp32 accumulator, as bf16 (8 elements per thread)
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_dq_finish_kernel(BwdParams p) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= (size_t)p.BH * p.N * D) return;
+  const float4 a = *reinterpret_cast<const float4*>(p.dqacc + i);
+  const float4 b = *reinterpret_cast<const float4*>(p.dqacc + i + 4);
+  u32x4_t w;
+  w[0] = pack_bf16x2(a.x * p.scale, a.y * p.scale);
+  w[1] = pack_bf16x2(a.z * p.scale, a.w * p.scale);
+  w[2] = pack_bf16x2(b.x * p.scale, b.y * p.scale);
+  w[3] = pack_bf16x2(b.z * p.scale, b.w * p.scale);
+  *reinterpret_cast<u32x4_t*>(p.dq + i) = w;
 }
 
 // ---- dK, dV: key blocks outside, query tiles inside ------------------------------
@@ -176,9 +203,14 @@ __device__ inline void decode_kblock(const BwdParams& p, int& bh, int& kb) {
 // One wavefront per SIMD: the dK and dV accumulators (32 keys × d each),
 // the K and V rows and two 32-row score tiles need more than the 256
 // registers a lane has when two wavefronts share a SIMD.
-template <int D, bool CAUSAL>
+// FUSED: also dQ, by the loop order of [15-779 L5] §7.4 — each step's dS goes
+// through LDS ([key][query] bf16), the next step multiplies it by the block's
+// K tile (kept in LDS) and adds the block's share of dQ to an fp32 buffer with
+// atomic adds.  Every wait then covers all outstanding memory operations.
+template <int D, bool CAUSAL, bool FUSED>
 __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
   using T = BwdTile<D>;
+  using TS = BwdTile<64>;  // the dS tile: 64 query columns (128-byte rows) per key
   constexpr int W = kBwdKvWaves;
   constexpr int BM = 64;              // query rows per step (two 32-row sub-tiles)
   constexpr int QT = BM * T::ROW;     // bytes of one Q (or dO) stage
@@ -191,6 +223,9 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   unsigned char* const qbufs[3] = {q_lds0, q_lds1, q_lds2};
   unsigned char* const obufs[3] = {o_lds0, o_lds1, o_lds2};
   float* const lbufs[3] = {l_lds0, l_lds1, l_lds2};
+  // FUSED: the block's K tile (tr reads give the B operand of dQ = dS K) and dS
+  __shared__ __attribute__((aligned(16))) unsigned char kt_lds[FUSED ? kBwdBlockK * T::ROW : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ds_lds[FUSED ? kBwdBlockK * BM * 2 : 16];
 
   int bh, kb;
   decode_kblock(p, bh, kb);
@@ -220,6 +255,29 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
 
   TileReads<D> rd;
   rd.init(lane);
+  // FUSED: this wavefront's share of dQ = dS K is d columns 32·dq_ds on, for
+  // both 32-query halves (d = 128) or for half dq_u0 (d = 64); the lane
+  // offsets of its transpose reads of K and dS (uniform indexes, computed once)
+  constexpr int DQ_NU = T::DSUB == 4 ? 2 : 1;
+  const int dq_ds = T::DSUB == 4 ? wave_u : wave_u >> 1;
+  const int dq_u0 = T::DSUB == 4 ? 0 : wave_u & 1;
+  int kt_o0 = 0, kt_o8 = 0, dso0[DQ_NU] = {}, dso8[DQ_NU] = {};
+  if constexpr (FUSED) {
+    kt_o0 = TileReads<D>::tr_off(lane, dq_ds, 0);
+    kt_o8 = TileReads<D>::tr_off(lane, dq_ds, 1);
+#pragma unroll
+    for (int iu = 0; iu < DQ_NU; ++iu) {
+      dso0[iu] = TileReads<64>::tr_off(lane, dq_u0 + iu, 0);
+      dso8[iu] = TileReads<64>::tr_off(lane, dq_u0 + iu, 1);
+    }
+    // the K rows of the block into kt_lds, swizzled like every tile
+    constexpr int RK = kBwdBlockK / T::RPR;  // 1 KiB runs
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
+    const int kgoff = run_goff<D>(wave_u % (16 / T::RPR), lane);
+#pragma unroll
+    for (int x = wave_u; x < RK; x += W)
+      load_lds16(krsrc, kt_lds + x * 1024, kgoff + k0 * T::ROW + (x - wave_u % (16 / T::RPR)) * 1024);
+  }
 
   const int first = CAUSAL ? k0 / BM : 0;  // query tiles before the block's first key see none of it
   const int n_steps = ceil_div(N, BM) - first;
@@ -242,7 +300,7 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
     if (wave_u == 1) load_lds4(lrsrc, lbufs[B] + 64, lane * 4 + (first + s) * BM * 8 + 256);
   };
   auto wait_stage = [&](bool more) {  // own loads of the oldest stage in flight have landed
-    if (!more)
+    if (FUSED || !more)
       wait_vmcnt<0>();
     else if (wave_u <= 1)
       wait_vmcnt<PER + 1>();
@@ -360,6 +418,45 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
       if (m + LC < 2 * NC) rc[m % LC] = op_c(m + LC);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (FUSED) {  // dS of the step into ds_lds: this lane's key row, 4 queries per write
+      const int krow = 32 * wave_u + i32;
+      unsigned char* rowp = ds_lds + krow * TS::ROW;
+      const int sz = TS::swz(krow);
+      // keys past N: their K rows read as zero, but P = exp(−L) there need not
+      // be finite, so their dS is cleared rather than multiplied by zero
+      const unsigned keep = key < N ? ~0u : 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<u32x2_t*>(rowp + (((4 * u + t) ^ sz) << 4) + 8 * g) =
+              u32x2_t{sw[2 * u + (t >> 1)][2 * (t & 1)] & keep, sw[2 * u + (t >> 1)][2 * (t & 1) + 1] & keep};
+    }
+  };
+  // FUSED: dQ rows of step s_prev (64 queries × d) += dS K over the block's keys;
+  // the wavefront takes 32 columns of d for both (d = 128) or one (d = 64) of
+  // the 32-row halves, then adds them into the fp32 buffer.
+  auto dq_phase = [&](int s_prev) __attribute__((always_inline)) {
+    f32x16_t a2[DQ_NU];
+#pragma unroll
+    for (int iu = 0; iu < DQ_NU; ++iu) a2[iu] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < kBwdBlockK / 16; ++kk) {
+      const bf16x8_t kb8 = TileReads<D>::tr_at(kt_lds, kt_o0, kt_o8, kk);
+#pragma unroll
+      for (int iu = 0; iu < DQ_NU; ++iu)
+        a2[iu] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TileReads<64>::tr_at(ds_lds, dso0[iu], dso8[iu], kk), kb8,
+                                                         a2[iu], 0, 0, 0);
+    }
+    const int qs = (first + s_prev) * BM;
+    float* dst = p.dqacc + ((size_t)bh * N) * D + dq_ds * 32 + i32;
+#pragma unroll
+    for (int iu = 0; iu < DQ_NU; ++iu)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = qs + 32 * (dq_u0 + iu) + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (row < N) __hip_atomic_fetch_add(dst + (size_t)row * D, a2[iu][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
   };
   // CLEAN: every query of the step comes at or after every key of the block.
   auto step = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
@@ -374,6 +471,10 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
       step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::false_type{});
     } else if (qs0 + BM - 1 >= kw) {  // else every query of the step precedes this wavefront's keys
       step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::true_type{});
+    } else if constexpr (FUSED) {     // ... and its dS rows are zero
+      unsigned char* rowp = ds_lds + (32 * wave_u + i32) * TS::ROW;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) *reinterpret_cast<u32x4_t*>(rowp + 16 * x) = u32x4_t{0, 0, 0, 0};
     }
   };
 
@@ -395,6 +496,12 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
     wait_stage(s + 1 < n_steps);
     block_barrier();  // stage s is in LDS for everyone; stage s-1's buffers are free
     if (s + 2 < n_steps) issue(s + 2, std::integral_constant<int, (B + 2) % 3>{});
+    if constexpr (FUSED) {
+      if (s > 0) {
+        dq_phase(s - 1);
+        block_barrier();  // everyone has read dS of step s-1 before step s writes its own
+      }
+    }
     step(s, buf, clean);
   };
   auto loop = [&](int s0, auto phase) __attribute__((always_inline)) {
@@ -415,6 +522,11 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
     loop(2, I2{});
   } else {
     loop(0, I0{});
+  }
+  if constexpr (FUSED) {
+    wait_vmcnt<0>();
+    block_barrier();  // dS of the last step is complete
+    dq_phase(n_steps - 1);
   }
 
   // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, one store each ------------------
@@ -658,7 +770,17 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
+  if (p.dqacc) {
+    static const hipError_t attr = allow_full_lds(&fa_bwd_dkdv_kernel<D, CAUSAL, true>);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, true>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n8 = rows * D / 8;
+    hipLaunchKernelGGL((fa_bwd_dq_finish_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);

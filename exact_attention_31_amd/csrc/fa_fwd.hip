@@ -502,14 +502,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  // static LDS above 64 KiB: allow the kernel the CU's 160 KiB in all
-  static const hipError_t attr = [] {
-    const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, SPARSE>);
-    hipFuncAttributes fa_attr;
-    const hipError_t e = hipFuncGetAttributes(&fa_attr, fn);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (int)fa_attr.sharedSizeBytes);
-  }();
+  static const hipError_t attr = allow_full_lds(&fa_fwd_kernel<D, CAUSAL, SPARSE>);
   if (attr != hipSuccess) return attr;
   const dim3 grid(p.BH * p.n_qblk);
   hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, SPARSE>), grid, dim3(kFwdThreads), 0, stream, p);

@@ -83,6 +83,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* ld;         // workspace [BH, N] pairs (L·log2 e, D = dO·O)
+  float* dqacc;      // null: dQ by its own pass; else workspace fp32 [BH, N, d] for atomic adds
   int BH;
   int N;
   int n_qblk;        // query blocks of kFwdBlockM rows (dQ kernel)
@@ -101,6 +102,17 @@ constexpr int kBwdBlockK = 32 * kBwdKvWaves;
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
 // divides the group size g = Hq / Hkv.
 __host__ __device__ inline int decode_group_width(int g) { return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
+
+// Static LDS beyond the default limit: let `kernel` use the CU's 160 KiB (once per
+// instantiation; the static size is read back from the code object).
+template <class K>
+hipError_t allow_full_lds(K* kernel) {
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  hipFuncAttributes attr;
+  const hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (int)attr.sharedSizeBytes);
+}
 
 hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, int causal, hipStream_t stream);

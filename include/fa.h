@@ -24,6 +24,8 @@
  *   fa_bwd     backward of fa_fwd: dQ, dK, dV from the saved O and L, with
  *              the probabilities recomputed rather than stored
  *              ([15-779 L5] §7; [pinghaoyang FA-1] "Backward").
+ *   fa_bwd_atomic  the same gradients in one key-block pass with dQ added up
+ *              atomically ([15-779 L5] §7.4): faster, not bit-reproducible.
  *
  * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
  * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
@@ -131,6 +133,26 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                  float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fa_bwd_atomic needs: the pairs of fa_bwd, padded
+ * to a multiple of 256 bytes, then an fp32 dQ accumulator [B, H, N, d].
+ * Returns 0 when the sizes are invalid. */
+size_t fa_bwd_atomic_workspace_bytes(int B, int H, int N, int d);
+
+/* The same backward in the loop order of [15-779 L5] §7.4 alone: one kernel
+ * walks the query tiles inside each key block and adds that block's share of
+ * dQ, dS K, into an fp32 accumulator with device-scope atomic adds; a last
+ * pass scales and rounds it into dq.  Five products per tile instead of seven,
+ * but the order of the additions into dQ follows the hardware's scheduling,
+ * so dq may differ between calls in its last bits (dk and dv do not).
+ * Arguments, layouts and errors as for fa_bwd, except:
+ *   workspace : at least fa_bwd_atomic_workspace_bytes(B, H, N, d) bytes,
+ *             16-byte aligned, owned by the caller; contents on entry ignored
+ *             (the accumulator is cleared by the call), on exit unspecified;
+ *             calls sharing it must be ordered. */
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fa_decode needs for these sizes: the per-split
  * partial results, fp32 [B, H, num_splits, d] then fp32 [B, H, num_splits].

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
                  "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes",
-                 "fa_fwd_block_sparse", "fa_decode_paged"):
+                 "fa_fwd_block_sparse", "fa_decode_paged", "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes"):
         assert want in names
 
 
@@ -149,6 +149,29 @@ def test_bwd_argument_checks():
     assert _bwd(dk=P[6]) == 8                               # two outputs on one buffer
     assert _bwd(ws=ctypes.c_void_p(0x50000000 + 16)) == 8   # workspace inside dO's range
     assert _lib().fa_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def _bwda(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, N=16, d=64,
+          scale=0.125, causal=1, ws=P[9], wsb=1 << 20):
+    return _lib().fa_bwd_atomic(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, ctypes.c_float(scale), causal, ws, wsb,
+                                None)
+
+
+def test_bwd_atomic_argument_checks():
+    """Same checks as fa_bwd; the workspace adds an fp32 [B, H, N, d] accumulator."""
+    assert _bwda(q=None) == 1 and _bwda(ws=None) == 6
+    assert _bwda(d=96) == 3 and _bwda(scale=float("inf")) == 5
+    assert _bwda(B=1 << 12, H=1 << 12, N=1 << 8) == 2
+    need = _lib().fa_bwd_atomic_workspace_bytes(1, 2, 16, 64)
+    assert need == 256 + 2 * 16 * 64 * 4                       # pairs padded to 256 bytes, then fp32 dQ
+    assert _lib().fa_bwd_atomic_workspace_bytes(1, 2, 16, 128) == 256 + 2 * 16 * 128 * 4
+    assert _lib().fa_bwd_atomic_workspace_bytes(1, 1, 33, 64) == 512 + 33 * 64 * 4
+    assert _bwda(wsb=need - 1) == 6
+    assert _bwda(d=128, wsb=need) == 6                          # d = 128 needs the larger buffer
+    assert _bwda(dq=P[1]) == 8 and _bwda(ws=ctypes.c_void_p(0x50000000 + 16)) == 8
+    assert _bwda(ws=MISALIGNED) == 4
+    assert _lib().fa_bwd_atomic_workspace_bytes(1, 1, 1, 80) == 0
+    assert _lib().fa_bwd_atomic_workspace_bytes(0, 1, 1, 64) == 0
 
 
 def _paged(q=P[0], kp=P[1], vp=P[2], o=P[3], lse=P[4], B=2, Hq=4, Hkv=2, d=64, ps=16, npg=8, tbl=P[5], mp=4,
