@@ -51,7 +51,12 @@ def parse():
                     help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
                          "decode and 'bwd' the backward, both measured after the step; 'copy' times a "
                          "plain 1 GiB device-to-device copy, the reference for scaling HBM byte counters")
+    ap.add_argument("--prefill", default=None, metavar="WORKLOAD",
+                    help="with --only fwd: time the forward on this synth workload instead (counter runs "
+                         "of other shapes, e.g. gpt2_small_causal_b8h12n1024d64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd-atomic", action="store_true",
+                    help="skip the fa_bwd_atomic comparison in the backward leg (counter runs of fa_bwd alone)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 --pmc (JSON), if present")
@@ -303,13 +308,30 @@ def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
     avg = sum(ms) / len(ms)
     flops = synth.bwd_flops(wf)
     tf = flops / (avg * 1e-3) / 1e12
-    return {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(avg, 4),
-            "ms_min": round(min(ms), 4), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "algorithmic_flops": flops,
-            "algorithmic_bytes": float(wf.B * wf.H * (16 * wf.N * wf.d + 4 * wf.N)),
-            "traffic": traffic_bytes(traffic, "bwd"),
-            "note": "three kernels per call (per-row L and D; dK, dV; dQ); the dQ pass recomputes S and dP, "
-                    "so the matrix cores run 7/5 of the counted FLOPs"}
+    res = {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(avg, 4),
+           "ms_min": round(min(ms), 4), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "algorithmic_flops": flops,
+           "algorithmic_bytes": float(wf.B * wf.H * (16 * wf.N * wf.d + 4 * wf.N)),
+           "traffic": traffic_bytes(traffic, "bwd"),
+           "note": "three kernels per call (per-row L and D; dK, dV; dQ); the dQ pass recomputes S and dP, "
+                   "so the matrix cores run 7/5 of the counted FLOPs"}
+    if args.no_bwd_atomic:
+        return res
+    # the one-pass form with atomic dQ, timed the same way for comparison
+    wsa = torch.empty(fa.fa_bwd_atomic_workspace_bytes(wf.B, wf.H, wf.N, wf.d), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        fa.fa_bwd_atomic(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=wsa)
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record()
+        fa.fa_bwd_atomic(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=wsa)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms_a = [e[0].elapsed_time(e[1]) for e in evs]
+    avg_a = sum(ms_a) / len(ms_a)
+    res["atomic"] = {"value": round(flops / (avg_a * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms": round(avg_a, 4),
+                     "note": "fa_bwd_atomic: one key-block pass, dQ added up with fp32 atomics"}
+    return res
 
 
 def main():
@@ -336,6 +358,11 @@ def main():
         return copy_reference(torch, dev, args)
 
     wf = synth.BY_NAME["llama3_8b_causal_b1h32n4096d128_kboost"]
+    if args.prefill:
+        if args.only != "fwd":
+            print("--prefill goes with --only fwd", file=sys.stderr)
+            return 2
+        wf = synth.BY_NAME[args.prefill]
     wd = synth.BY_NAME["decode_b16h32_lkv32768_d128_s64"]
     do_f = args.only in ("all", "fwd")
     do_d = args.only in ("all", "decode")
@@ -417,10 +444,12 @@ def main():
         tf = flops / (f_avg * 1e-3) / 1e12
         out["prefill"] = {"ms": round(f_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tf, 2),
                           "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-        out["roofline"] = {"kernel": "fa_fwd_kernel<128,true>", "bound": "mfma", "achieved": round(tf, 2),
+        out["roofline"] = {"kernel": f"fa_fwd_kernel<{wf.d},{str(wf.causal).lower()}>", "bound": "mfma",
+                           "achieved": round(tf, 2),
                            "peak": round(MFMA_BF16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                           "traffic": traffic_bytes(traffic, "fwd"), "algorithmic_bytes": fbytes}
+                           "traffic": None if args.prefill else traffic_bytes(traffic, "fwd"),
+                           "algorithmic_bytes": fbytes}
     if d_avg:
         gbs = dbytes / (d_avg * 1e-3) / 1e9
         out["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4), "ms_min": round(min(dec_ms), 4),

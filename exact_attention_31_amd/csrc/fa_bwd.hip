@@ -18,10 +18,16 @@
 //                 its 128 keys in registers and writes them once;
 //   fa_bwd_dq     query blocks outside, key/value tiles inside, as in the
 //                 forward: dQ of 256 query rows stays in registers.
-// dQ is not accumulated with atomic adds from the key-block kernel (the
-// scheme of [15-779 L5] §7.4); its own pass recomputes S and dP instead,
+// By default dQ is not accumulated with atomic adds from the key-block kernel
+// (the scheme of [15-779 L5] §7.4); its own pass recomputes S and dP instead,
 // which costs two more tile products (seven in all, against five) but keeps
 // the result deterministic and needs no fp32 dQ buffer or atomic traffic.
+// The atomic scheme is built too (fa_bwd_dkdv<FUSED>, then fa_bwd_dq_finish):
+// each key block adds its dQ share into an fp32 buffer, and every key block
+// of a head adds into all of the head's later query rows, so the atomic
+// traffic is about N/128 times the size of dQ in fp32.  On this chip those
+// device-scope fp32 adds, not the products, bound it: at 4096 keys the atomic
+// form takes about twice as long as the two-pass form.
 //
 // Layout on chip (64-lane wavefronts, v_mfma_f32_32x32x16_bf16):
 // * dkdv: each wavefront owns 32 keys.  The products are taken so that a
