@@ -251,12 +251,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   // L: rows with few keys need it within 1e-3) and ℓ_b of the bf16-rounded P̃
   // that enter the MFMA (for O: numerator and denominator then use the same
   // weights, so a row dominated by one key returns that key's value exactly).
-  float l = 0.f, lb = 0.f;
+  float l = 0.f;
+  float lb[2] = {0.f, 0.f};  // ℓ_b in two partial sums, accumulated in the matrix phase
   f32x16_t acc[T::DSUB];
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
   f32x16_t s[T::NSUB];       // scores of the tile between its QK and its softmax
-  u32x4_t pw[T::KS_PV];      // P̃ of the tile between its softmax and its PV
+  bf16x2_t pw[T::KS_PV][4];  // P̃ of the tile between its softmax and its PV (bf16 pairs)
 
   // ---- softmax phase of tile j: mask, row max, rescale, P̃ and the sums ------------
   auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
@@ -274,13 +275,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     // P̃ against the current reference max; the tile sum bounds every element,
     // so a sum at most 2^kRescaleLog2 proves that no row outgrew m by more
     // than that and the row max is not needed.
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs, rsb;
+    float rs;
     auto exps = [&]() __attribute__((always_inline)) {
       // SPARSE: a row may still have no key (m = −∞); 0 then stands in for
       // the offset, which keeps masked logits at weight 0 instead of NaN
       const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
-      float r2[2] = {0.f, 0.f}, rb2[2] = {0.f, 0.f};
+      float r2[2] = {0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < T::KS_PV; ++kk) {
         const int h8 = (kk & 1) * 8;
@@ -289,17 +289,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e], c, -mc));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][h8 + 2 * e + 1], c, -mc));
           r2[e & 1] += e0 + e1;
-          // The pair goes to dot2 directly: fed from an element of the packed
-          // u32x4 instead, hipcc (ROCm 7.2) reads element 0 four times.
-          bf16x2_t pe;
-          pe[0] = (__bf16)e0;
-          pe[1] = (__bf16)e1;
-          rb2[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rb2[e & 1], false);
-          pw[kk][e] = __builtin_bit_cast(uint32_t, pe);
+          pw[kk][e][0] = (__bf16)e0;
+          pw[kk][e][1] = (__bf16)e1;
         }
       }
       rs = r2[0] + r2[1];
-      rsb = rb2[0] + rb2[1];
     };
     exps();
     if (__any(!(rs <= kSumBound) || (SPARSE && m == -INFINITY))) {  // also taken for inf / NaN sums (first tile: m = -inf)
@@ -318,7 +312,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
         const float m_new = fmaxf(m, mt);
         const float alpha = (SPARSE && m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
         l *= alpha;
-        lb *= alpha;
+        lb[0] *= alpha;
+        lb[1] *= alpha;
 #pragma unroll
         for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
         m = m_new;
@@ -326,7 +321,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       }
     }
     l += rs;
-    lb += rsb;
   };
 
   // ---- matrix phase: Oᵀ += Vᵀ_j P̃ᵀ_j and Sᵀ_{j+1} = K_{j+1} Qᵀ, MFMAs interleaved ------
@@ -335,13 +329,27 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + k_rd[kk] + sub * 32 * T::ROW);
     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], s[sub], 0, 0, 0);
   };
+  // ℓ_b += the bf16 P̃ of k-step kk.  v_dot2 shares the matrix core's pipe: in
+  // the softmax phase each one would wait for the other wavefront's MFMA, here
+  // it queues behind this wavefront's own.  ℓ_b and the accumulator take the
+  // same tile in the same phase, so a later rescale treats them alike.
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // (The pairs are kept as bf16x2 values: taken as elements of a packed u32x4,
+  // hipcc (ROCm 7.2) feeds all four dot2 of a k-step from element 0.)
+  auto lb_step = [&](int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lb[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[kk][e], ones, lb[e & 1], false);
+  };
   auto pv_step = [&](const unsigned char* vb, int i) __attribute__((always_inline)) {
     const int kk = i / T::DSUB, ds = i % T::DSUB;
     const u32x2_t a0 = lds_tr_read(vb, v_rd[ds] + 16 * kk * T::ROW);
     const u32x2_t a1 = lds_tr_read(vb, v_rd[ds] + (16 * kk + 8) * T::ROW);
     const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-    acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, pw[kk]), acc[ds], 0, 0, 0);
+    const bf16x8_t pb = __builtin_shufflevector(__builtin_shufflevector(pw[kk][0], pw[kk][1], 0, 1, 2, 3),
+                                                __builtin_shufflevector(pw[kk][2], pw[kk][3], 0, 1, 2, 3), 0, 1, 2,
+                                                3, 4, 5, 6, 7);
+    acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[ds], 0, 0, 0);
+    if (ds == T::DSUB - 1) lb_step(kk);
   };
   constexpr int NQK = T::KS_QK * T::NSUB;  // MFMAs of one Sᵀ tile
   constexpr int NPV = T::KS_PV * T::DSUB;  // MFMAs of one Oᵀ update
@@ -371,6 +379,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    asm volatile("" : "+v"(lb[0]), "+v"(lb[1]));  // the dot2 stay in this phase
     __builtin_amdgcn_s_setprio(0);
   };
   auto matrix = [&](const unsigned char* vb, const unsigned char* kb, bool do_pv, bool do_qk) __attribute__((always_inline)) {
@@ -383,6 +392,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     if (do_pv) {
 #pragma unroll
       for (int i = 0; i < NPV; ++i) pv_step(vb, i);
+      asm volatile("" : "+v"(lb[0]), "+v"(lb[1]));
     }
   };
 
@@ -482,9 +492,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
 
   // ---- epilogue: one division, one store of O and L ------------------------------
   l = pair_sum(l);
-  lb = pair_sum(lb);
+  const float lbs = pair_sum(lb[0] + lb[1]);
   if (q_row < N) {
-    const float inv = (SPARSE && lb == 0.f) ? 0.f : 1.f / lb;  // SPARSE: a row with no key writes O = 0, L = −∞
+    const float inv = (SPARSE && lbs == 0.f) ? 0.f : 1.f / lbs;  // SPARSE: a row with no key writes O = 0, L = −∞
     uint16_t* orow = p.o + base + (size_t)q_row * D;
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds)
