@@ -491,23 +491,38 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   if (grp == 0) block_barrier();
 
   // ---- epilogue: one division, one store of O and L ------------------------------
+  // O leaves the accumulators as 8-byte pieces of 32 different rows per
+  // instruction; written to HBM like that, each row segment is a separate
+  // partial-line write.  The wavefront stages its 32 rows in LDS instead (a K
+  // or V buffer: every wavefront is past its last read of them) and writes
+  // them back as whole rows, 16 bytes a lane.
   l = pair_sum(l);
   const float lbs = pair_sum(lb[0] + lb[1]);
-  if (q_row < N) {
-    const float inv = (SPARSE && lbs == 0.f) ? 0.f : 1.f / lbs;  // SPARSE: a row with no key writes O = 0, L = −∞
-    uint16_t* orow = p.o + base + (size_t)q_row * D;
+  const float inv = (SPARSE && lbs == 0.f) ? 0.f : 1.f / lbs;  // SPARSE: a row with no key writes O = 0, L = −∞
+  constexpr int SROW = 2 * D + 16;  // padded row stride of the staging tile (bytes)
+  static_assert(32 * SROW <= T::TILE_BYTES, "a wavefront's rows fit one tile buffer");
+  unsigned char* const stg = wave_u == 0 ? k_lds0 : wave_u == 1 ? k_lds1 : wave_u == 2 ? k_lds2 : wave_u == 3 ? k_lds3
+                           : wave_u == 4 ? v_lds0 : wave_u == 5 ? v_lds1 : wave_u == 6 ? v_lds2 : v_lds3;
 #pragma unroll
-    for (int ds = 0; ds < T::DSUB; ++ds)
+  for (int ds = 0; ds < T::DSUB; ++ds)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = ds * 32 + r4 * 8 + g * 4;
-        u32x2_t w;
-        w[0] = pack_bf16x2(acc[ds][4 * r4 + 0] * inv, acc[ds][4 * r4 + 1] * inv);
-        w[1] = pack_bf16x2(acc[ds][4 * r4 + 2] * inv, acc[ds][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + d0) = w;
-      }
-    if (g == 0) p.lse[(size_t)bh * N + q_row] = m * p.scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = ds * 32 + r4 * 8 + g * 4;
+      u32x2_t w;
+      w[0] = pack_bf16x2(acc[ds][4 * r4 + 0] * inv, acc[ds][4 * r4 + 1] * inv);
+      w[1] = pack_bf16x2(acc[ds][4 * r4 + 2] * inv, acc[ds][4 * r4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(stg + i32 * SROW + 2 * d0) = w;
+    }
+  constexpr int RPI = 64 / T::CH;  // rows per store instruction
+  const int rr0 = lane / T::CH, cc = lane % T::CH;
+  u32x4_t ow[32 / RPI];
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) ow[it] = *reinterpret_cast<const u32x4_t*>(stg + (it * RPI + rr0) * SROW + cc * 16);
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it)
+    if (wq0 + it * RPI + rr0 < N)
+      *reinterpret_cast<u32x4_t*>(p.o + base + (size_t)(wq0 + it * RPI + rr0) * D + cc * 8) = ow[it];
+  if (q_row < N && g == 0) p.lse[(size_t)bh * N + q_row] = m * p.scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
