@@ -148,6 +148,39 @@ __device__ inline bf16x8_t pack8(const float* x) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// Writes a wavefront's 32 output rows, held as fp32 accumulators whose lane is
+// the row (a[ds] element r: column 32·ds + 8·(r/4) + 4·g + r%4), scaled by
+// `mul` and rounded to bf16.  Stored straight from that layout, every store
+// instruction would write 8-byte pieces of 32 rows; instead the rows go
+// through `stg` (32·2D bytes of LDS that nothing else uses meanwhile; 16-byte
+// chunks XOR-swizzled by the row) and leave as whole rows, 16 bytes a lane.
+// Rows at or past `valid` are not written.
+template <int D>
+__device__ inline void store_rows_staged(const f32x16_t (&a)[D / 32], float mul, unsigned char* stg,
+                                         uint16_t* out, int valid, int lane) {
+  constexpr int CH = D / 8, ROW = 2 * D, RPI = 64 / CH;
+  const int i32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(a[ds][4 * r4 + 0] * mul, a[ds][4 * r4 + 1] * mul);
+      w[1] = pack_bf16x2(a[ds][4 * r4 + 2] * mul, a[ds][4 * r4 + 3] * mul);
+      *reinterpret_cast<u32x2_t*>(stg + i32 * ROW + (((4 * ds + r4) ^ (i32 % CH)) << 4) + 8 * g) = w;
+    }
+  const int rr0 = lane / CH, cc = lane % CH;
+  u32x4_t ow[32 / RPI];
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + rr0;
+    ow[it] = *reinterpret_cast<const u32x4_t*>(stg + rr * ROW + ((cc ^ (rr % CH)) << 4));
+  }
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it)
+    if (it * RPI + rr0 < valid) *reinterpret_cast<u32x4_t*>(out + (size_t)(it * RPI + rr0) * D + cc * 8) = ow[it];
+}
+
 // ---- per-row statistics: (L·log2 e, D = dO·O) ---------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
@@ -536,22 +569,17 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   }
 
   // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, one store each ------------------
-  if (key < N) {
-    uint16_t* krow = p.dk + base + (size_t)key * D;
-    uint16_t* vrow = p.dv + base + (size_t)key * D;
-#pragma unroll
-    for (int ds = 0; ds < T::DSUB; ++ds)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = ds * 32 + r4 * 8 + g * 4;
-        u32x2_t w;
-        w[0] = pack_bf16x2(dk[ds][4 * r4 + 0] * p.scale, dk[ds][4 * r4 + 1] * p.scale);
-        w[1] = pack_bf16x2(dk[ds][4 * r4 + 2] * p.scale, dk[ds][4 * r4 + 3] * p.scale);
-        *reinterpret_cast<u32x2_t*>(krow + d0) = w;
-        w[0] = pack_bf16x2(dv[ds][4 * r4 + 0], dv[ds][4 * r4 + 1]);
-        w[1] = pack_bf16x2(dv[ds][4 * r4 + 2], dv[ds][4 * r4 + 3]);
-        *reinterpret_cast<u32x2_t*>(vrow + d0) = w;
-      }
+  // staged in the Q and dO stage buffers, free once every wavefront is past
+  // its last step: 32 rows × 2D bytes per region, two regions per buffer
+  block_barrier();
+  {
+    constexpr int RG = 32 * T::ROW;
+    static_assert(2 * RG == QT, "two staging regions per stage buffer");
+    unsigned char* const kst = wave_u == 0 ? q_lds0 : wave_u == 1 ? q_lds0 + RG : wave_u == 2 ? q_lds1 : q_lds1 + RG;
+    unsigned char* const vst = wave_u == 0 ? q_lds2 : wave_u == 1 ? q_lds2 + RG : wave_u == 2 ? o_lds0 : o_lds0 + RG;
+    const int valid = min(32, N - kw);
+    store_rows_staged<D>(dk, p.scale, kst, p.dk + base + (size_t)kw * D, valid, lane);
+    store_rows_staged<D>(dv, 1.f, vst, p.dv + base + (size_t)kw * D, valid, lane);
   }
 }
 
@@ -753,18 +781,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
     if (j + 2 < n_tiles) body(j + 2, I2{}, G{});
   }
 
-  if (q_row < N) {
-    uint16_t* row = p.dq + base + (size_t)q_row * D;
-#pragma unroll
-    for (int ds = 0; ds < T::DSUB; ++ds)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = ds * 32 + r4 * 8 + g * 4;
-        u32x2_t w;
-        w[0] = pack_bf16x2(dq[ds][4 * r4 + 0] * p.scale, dq[ds][4 * r4 + 1] * p.scale);
-        w[1] = pack_bf16x2(dq[ds][4 * r4 + 2] * p.scale, dq[ds][4 * r4 + 3] * p.scale);
-        *reinterpret_cast<u32x2_t*>(row + d0) = w;
-      }
+  // dQ staged in the K/V stage buffers (free once every wavefront is past its
+  // last tile), two 32-row regions per buffer
+  block_barrier();
+  {
+    constexpr int RG = 32 * T::ROW;
+    static_assert(2 * RG == KT, "two staging regions per stage buffer");
+    unsigned char* const st = wave_u == 0 ? k_lds0 : wave_u == 1 ? k_lds0 + RG : wave_u == 2 ? k_lds1
+                            : wave_u == 3 ? k_lds1 + RG : wave_u == 4 ? k_lds2 : wave_u == 5 ? k_lds2 + RG
+                            : wave_u == 6 ? v_lds0 : v_lds0 + RG;
+    if (wq0 < N) store_rows_staged<D>(dq, p.scale, st, p.dq + base + (size_t)wq0 * D, min(32, N - wq0), lane);
   }
 }
 
