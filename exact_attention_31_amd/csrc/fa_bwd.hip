@@ -324,22 +324,31 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   // runs first, then dO); the lane's offset is the same for all of them.
   const int x0 = wave_u % R;
   const int goff = run_goff<D>(x0, lane);
-  auto issue = [&](int s, auto buf) __attribute__((always_inline)) {
+  // Stages past the last one are loaded all the same: their rows lie past N
+  // and read as zeros into a buffer nobody reads again, and every step then
+  // keeps the same number of loads in flight.
+  auto issue_tile = [&](int s, auto buf, int i) __attribute__((always_inline)) {  // load i < PER of stage s
     constexpr int B = decltype(buf)::value;
     const int toff = (first + s) * QT;  // byte offset of the stage's first row
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = wave_u + i * W;  // uniform
-      if (x < R)
-        load_lds16(qrsrc, qbufs[B] + x * 1024, goff + toff + (x - x0) * 1024);
-      else
-        load_lds16(orsrc, obufs[B] + (x - R) * 1024, goff + toff + (x - R - x0) * 1024);
-    }
+    const int x = wave_u + i * W;       // i < R / W exactly when x < R (W divides R)
+    if (i * W < R)
+      load_lds16(qrsrc, qbufs[B] + x * 1024, goff + toff + (x - x0) * 1024);
+    else
+      load_lds16(orsrc, obufs[B] + (x - R) * 1024, goff + toff + (x - R - x0) * 1024);
+  };
+  auto issue_ld = [&](int s, auto buf) __attribute__((always_inline)) {  // the stage's (L, D) pairs
+    constexpr int B = decltype(buf)::value;
     if (wave_u == 0) load_lds4(lrsrc, lbufs[B], lane * 4 + (first + s) * BM * 8);
     if (wave_u == 1) load_lds4(lrsrc, lbufs[B] + 64, lane * 4 + (first + s) * BM * 8 + 256);
   };
-  auto wait_stage = [&](bool more) {  // own loads of the oldest stage in flight have landed
-    if (FUSED || !more)
+  auto issue = [&](int s, auto buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) issue_tile(s, buf, i);
+    issue_ld(s, buf);
+  };
+  static_assert(R % W == 0, "a load's tensor does not depend on the wavefront");
+  auto wait_stage = [&]() {  // own loads of the oldest stage in flight have landed
+    if (FUSED)
       wait_vmcnt<0>();
     else if (wave_u <= 1)
       wait_vmcnt<PER + 1>();
@@ -370,8 +379,10 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   static_assert(16 % NA == 0 && 16 % NC == 0 && LA <= NA && LC <= NC, "phase shapes");
   f32x16_t sacc[2], dpacc[2];
   u32x4_t pw[4], sw[4];  // bf16 P and dS: the B operands of the four k-steps
+  // issue_next(i): tile load i of the stage two steps ahead, one after each
+  // of the first PER MFMAs (the matrix core keeps running while they issue)
   auto step_body = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, int qs0,
-                       auto masked) __attribute__((always_inline)) {
+                       auto masked, auto issue_next) __attribute__((always_inline)) {
     // operand j of A/B: sub-tile j / NA, k-step (j % NA) / 2, Q (even j) or dO (odd j)
     auto op_a = [&](int j) __attribute__((always_inline)) {
       return rd.rows((j & 1) ? ob : qb, (j % NA) >> 1, j / NA);
@@ -425,10 +436,12 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
 #pragma unroll
     for (int j = 0; j < LA; ++j) ra[j] = op_a(j);
     __builtin_amdgcn_sched_barrier(0);
+    static_assert(PER <= NA, "the stage loads fit phase A");
 #pragma unroll
     for (int j = 0; j < NA; ++j) {  // A
       mfma_a(j, ra[j % LA]);
       ra[j % LA] = op_a(j + LA);
+      if (j < PER) issue_next(j);
       if (j == NA - 1) read_ld(1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -501,19 +514,26 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   auto step = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     const int qs0 = (first + s) * BM;
+    auto issue_next = [&](int i) __attribute__((always_inline)) {
+      issue_tile(s + 2, std::integral_constant<int, (B + 2) % 3>{}, i);
+    };
     // lane offsets opaque here: addresses are formed as offset + constant
 #pragma unroll
     for (int kk = 0; kk < T::KS; ++kk) asm volatile("" : "+v"(rd.row[kk]));
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(rd.tr0[ds]), "+v"(rd.tr8[ds]));
     if (decltype(clean)::value) {
-      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::false_type{});
+      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::false_type{}, issue_next);
     } else if (qs0 + BM - 1 >= kw) {  // else every query of the step precedes this wavefront's keys
-      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::true_type{});
-    } else if constexpr (FUSED) {     // ... and its dS rows are zero
-      unsigned char* rowp = ds_lds + (32 * wave_u + i32) * TS::ROW;
+      step_body(qbufs[B], obufs[B], lbufs[B], qs0, std::true_type{}, issue_next);
+    } else {                          // ... (the stage loads are still this wavefront's share)
 #pragma unroll
-      for (int x = 0; x < 8; ++x) *reinterpret_cast<u32x4_t*>(rowp + 16 * x) = u32x4_t{0, 0, 0, 0};
+      for (int i = 0; i < PER; ++i) issue_next(i);
+      if constexpr (FUSED) {          // ... and its dS rows are zero
+        unsigned char* rowp = ds_lds + (32 * wave_u + i32) * TS::ROW;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) *reinterpret_cast<u32x4_t*>(rowp + 16 * x) = u32x4_t{0, 0, 0, 0};
+      }
     }
   };
 
@@ -523,8 +543,8 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   using Y = std::true_type;
   using G = std::false_type;
   issue(0, I0{});
-  if (n_steps > 1) issue(1, I1{});
-  wait_stage(n_steps > 1);
+  issue(1, I1{});
+  wait_stage();
   // K and V were loaded before the stages, so they are in: settle the
   // compiler's load tracking for them once, outside the loop.
 #pragma unroll
@@ -532,9 +552,9 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, kf[kk])), "v"(__builtin_bit_cast(u32x4_t, vf[kk])));
   auto body = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
-    wait_stage(s + 1 < n_steps);
+    wait_stage();
     block_barrier();  // stage s is in LDS for everyone; stage s-1's buffers are free
-    if (s + 2 < n_steps) issue(s + 2, std::integral_constant<int, (B + 2) % 3>{});
+    issue_ld(s + 2, std::integral_constant<int, (B + 2) % 3>{});  // its tiles: during the step
     if constexpr (FUSED) {
       if (s > 0) {
         dq_phase(s - 1);
@@ -570,7 +590,9 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
 
   // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, one store each ------------------
   // staged in the Q and dO stage buffers, free once every wavefront is past
-  // its last step: 32 rows × 2D bytes per region, two regions per buffer
+  // its last step and the loads past the last stage have landed: 32 rows ×
+  // 2D bytes per region, two regions per buffer
+  wait_vmcnt<0>();
   block_barrier();
   {
     constexpr int RG = 32 * T::ROW;
