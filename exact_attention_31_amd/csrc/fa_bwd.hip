@@ -665,24 +665,24 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
 
   const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
   const int goff = run_goff<D>(wave_u % R, lane);
-  auto issue = [&](int j, auto buf) __attribute__((always_inline)) {
+  // Tiles past the last are loaded all the same, from past the end of K and V
+  // (zeros, no memory traffic) into a buffer nobody reads again, and every
+  // step then keeps the same number of loads in flight.
+  auto issue_tile = [&](int j, auto buf, int i) __attribute__((always_inline)) {  // load i < PER of tile j
     constexpr int B = decltype(buf)::value;
-    const int toff = j * KT;  // byte offset of the tile's first row
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = wave_u + i * kFwdWaves;
-      if (x < R)
-        load_lds16(krsrc, kbufs[B] + x * 1024, goff + toff + (x - wave_u % R) * 1024);
-      else
-        load_lds16(vrsrc, vbufs[B] + (x - R) * 1024, goff + toff + (x - R - wave_u % R) * 1024);
-    }
-  };
-  auto wait_stage = [&](bool more) {
-    if (more)
-      wait_vmcnt<PER>();
+    const int toff = j < n_tiles ? j * KT : N * T::ROW;  // byte offset of the tile's first row
+    const int x = wave_u + i * kFwdWaves;  // i < R / 8 exactly when x < R (8 divides R)
+    if (i * kFwdWaves < R)
+      load_lds16(krsrc, kbufs[B] + x * 1024, goff + toff + (x - wave_u % R) * 1024);
     else
-      wait_vmcnt<0>();
+      load_lds16(vrsrc, vbufs[B] + (x - R) * 1024, goff + toff + (x - R - wave_u % R) * 1024);
   };
+  static_assert(R % kFwdWaves == 0, "a load's tensor does not depend on the wavefront");
+  auto issue = [&](int j, auto buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) issue_tile(j, buf, i);
+  };
+  auto wait_stage = [&]() { wait_vmcnt<PER>(); };  // the oldest tile in flight has landed
 
   f32x16_t dq[T::DSUB];
 #pragma unroll
@@ -691,11 +691,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;  // last key this row sees
 
   // CLEAN: every row of the workgroup sees every key of the tile (no mask, no skip)
+  // issue_next(i): load i of the tile two steps ahead, one after each of the
+  // first PER MFMAs of a clean step (before the step otherwise)
   auto step = [&](int j, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     constexpr bool CLEAN = decltype(clean)::value;
+    auto issue_next = [&](int i) __attribute__((always_inline)) {
+      issue_tile(j + 2, std::integral_constant<int, (B + 2) % 3>{}, i);
+    };
     const int kv0 = j * BN;
-    if (!CLEAN && CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
+    if (!CLEAN) {  // tiles with a mask or a skip: the loads go out first
+#pragma unroll
+      for (int i = 0; i < PER; ++i) issue_next(i);
+      if (CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
+    }
     const unsigned char* kb = kbufs[B];
     const unsigned char* vb = vbufs[B];
     // lane offsets opaque here: addresses are formed as offset + constant
@@ -741,10 +750,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
 #pragma unroll
     for (int t = 0; t < LA; ++t) ra[t] = op_a(t);
     __builtin_amdgcn_sched_barrier(0);
+    static_assert(PER <= NA, "the tile loads fit phase A");
 #pragma unroll
     for (int t = 0; t < NA; ++t) {  // A
       mfma_a(t, ra[t % LA]);
       ra[t % LA] = op_a(t + LA);
+      if (CLEAN && t < PER) issue_next(t);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -774,17 +785,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   issue(0, I0{});
-  if (n_tiles > 1) issue(1, I1{});
-  wait_stage(n_tiles > 1);
+  issue(1, I1{});
+  wait_stage();
 #pragma unroll
   for (int kk = 0; kk < T::KS; ++kk)
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[kk])), "v"(__builtin_bit_cast(u32x4_t, of[kk])));
   asm volatile("" ::"v"(ld.x), "v"(ld.y));
   auto body = [&](int j, auto buf, auto clean) __attribute__((always_inline)) {
-    constexpr int B = decltype(buf)::value;
-    wait_stage(j + 1 < n_tiles);
-    block_barrier();
-    if (j + 2 < n_tiles) issue(j + 2, std::integral_constant<int, (B + 2) % 3>{});
+    wait_stage();
+    block_barrier();  // tile j is in LDS for everyone; tile j-1's buffers are free
     step(j, buf, clean);
   };
   using Y = std::true_type;
@@ -804,7 +813,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   }
 
   // dQ staged in the K/V stage buffers (free once every wavefront is past its
-  // last tile), two 32-row regions per buffer
+  // last tile and the loads past the last tile have landed), two 32-row
+  // regions per buffer
+  wait_vmcnt<0>();
   block_barrier();
   {
     constexpr int RG = 32 * T::ROW;
