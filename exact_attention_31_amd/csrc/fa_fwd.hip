@@ -158,24 +158,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   const size_t base = (size_t)bh * N * D;
   const int grp = wave_u >> 2;  // wavefronts w and w+4 share a SIMD and alternate phases
 
-  // Direct global->LDS loads, issued by the four wavefronts of group 1:
-  // wavefront w (w & 3 = u), load i fills LDS chunk slots (i*4 + u)*64 + lane
-  // of the tile; the slot's (row, swizzled chunk) names the global chunk this
-  // lane fetches.  Load i covers rows r0 + i*RPL, and both swizzles repeat
-  // with that period, so load i is load 0 shifted by i*RPL rows.  Rows past N
-  // lie past the head's bytes and read as zero (their logits are masked).
-  constexpr int RPL = (kFwdWaves / 2) * 64 / T::CH;  // rows covered by one load across group 1
+  // Direct global->LDS loads, a tile issued by the four wavefronts of a group
+  // (K by group 0, V by group 1): wavefront w (w & 3 = u), load i fills LDS
+  // chunk slots (i*4 + u)*64 + lane of the tile; the slot's (row, swizzled
+  // chunk) names the global chunk this lane fetches.  Load i covers rows
+  // r0 + i*RPL, and both swizzles repeat with that period, so load i is load 0
+  // shifted by i*RPL rows.  Rows past N lie past the head's bytes and read as
+  // zero (their logits are masked).
+  constexpr int RPL = (kFwdWaves / 2) * 64 / T::CH;  // rows covered by one load across a group
   const int r0 = ((wave & 3) * 64 + lane) / T::CH;
   const int cpos = lane % T::CH;
   const int k_goff = r0 * T::ROW + ((cpos ^ T::k_swz(r0)) << 4);
   const int v_goff = r0 * T::ROW + ((cpos ^ T::v_swz(r0)) << 4);
   const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int goff, int kv0, unsigned char* dst) {
-    unsigned char* d = dst + (wave_u & 3) * 1024;
-#pragma unroll
-    for (int i = 0; i < 2 * T::LOADS; ++i) load_lds16(rsrc, d + i * (kFwdWaves / 2) * 1024, goff + (kv0 + i * RPL) * T::ROW);
-  };
 
   // Operand-read lane offsets (bytes within a tile).
   int k_rd[T::KS_QK];  // K rows i32 (+32 per sub-tile), chunk 2kk + g
@@ -403,40 +399,31 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   // Sᵀ_{j+1} = K_{j+1} Qᵀ.  Group 1 (wavefronts 4-7) starts one barrier later
   // than group 0, so the two wavefronts of a SIMD are always in opposite
   // phases: one feeds the matrix core while the other runs the softmax.
-  // Only group 1 loads, and only in its softmax phases, so the matrix phases
-  // never issue or wait for a load.  With T the global phase (group 0's
-  // phase index; group 1's plus one), batch b (K_{b+4}, V_{b+3}) is issued at
-  // the start of group 1's Y(b), T = 2b+2, into the buffers that K_b and
-  // V_{b-1} left at T = 2b+1; group 1 waits for it at the end of its Y(b+2),
-  // T = 2b+6, before group 0's X(b+3) reads it at T = 2b+8.
+  // The K tiles stream through group 0 and the V tiles through group 1, each
+  // issuing its loads at the start of its softmax phases, so the matrix
+  // phases never issue or wait for a load.  With T the global phase (group
+  // 0's phase index; group 1's plus one), Y(j) loads tile j+3: group 0's at
+  // T = 2j+1 puts K_{j+3} where K_{j-1} was (last read at T = 2j-1), group 1's
+  // at T = 2j+2 puts V_{j+3} where V_{j-1} was (last read at T = 2j+1).  At
+  // the end of Y(j) a wavefront waits for its tile j+1, which the matrix
+  // phases read from T = 2j+2 (K) and T = 2j+4 (V) on.  Tiles outside
+  // [0, n_tiles) are loaded from past the end of K and V (zeros, no memory
+  // traffic) into buffers nobody reads again, so every wavefront keeps the
+  // same number of loads in flight.
   auto kb = [&](int j) { return kbufs[j & 3]; };
   auto vb = [&](int j) { return vbufs[j & 3]; };
-  auto batch_tiles = [&](int b) { return (b + 4 < n_tiles ? 1 : 0) + (b + 3 >= 0 && b + 3 < n_tiles ? 1 : 0); };
-  auto wait_batches = [&](int pending) {  // at most `pending` tiles of loads outstanding
-    if (pending >= 4)
-      wait_vmcnt<8 * T::LOADS>();
-    else if (pending == 3)
-      wait_vmcnt<6 * T::LOADS>();
-    else if (pending == 2)
-      wait_vmcnt<4 * T::LOADS>();
-    else if (pending == 1)
-      wait_vmcnt<2 * T::LOADS>();
-    else
-      wait_vmcnt<0>();
-  };
-  auto issue_batch = [&](int b, auto phase) __attribute__((always_inline)) {
-    constexpr int P = decltype(phase)::value;  // b mod 4
-    if (b + 4 < n_tiles) load_tile(krsrc, k_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 4)), kb(P));
-    if (b + 3 < n_tiles) load_tile(vrsrc, v_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 3)), vb(P + 3));
-  };
-  if (grp == 1) {
+  const __amdgpu_buffer_rsrc_t mrsrc = grp ? vrsrc : krsrc;
+  const int m_goff = grp ? v_goff : k_goff;
+  auto load_tile = [&](int t, unsigned char* dst) __attribute__((always_inline)) {  // this group's tile t
+    const int kv0 = (t >= 0 && t < n_tiles) ? __builtin_amdgcn_readfirstlane(tile_kv0(t)) : N;
+    unsigned char* d = dst + (wave_u & 3) * 1024;
 #pragma unroll
-    for (int b = -4; b < 0; ++b) {
-      if (b + 4 < n_tiles) load_tile(krsrc, k_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 4)), kb(b + 4));
-      if (b + 3 >= 0 && b + 3 < n_tiles) load_tile(vrsrc, v_goff, __builtin_amdgcn_readfirstlane(tile_kv0(b + 3)), vb(b + 3));
-    }
-  }
-  wait_batches(batch_tiles(-3) + batch_tiles(-2) + batch_tiles(-1));
+    for (int i = 0; i < 2 * T::LOADS; ++i)
+      load_lds16(mrsrc, d + i * (kFwdWaves / 2) * 1024, m_goff + (kv0 + i * RPL) * T::ROW);
+  };
+#pragma unroll
+  for (int t = 0; t < 3; ++t) load_tile(t, grp ? vbufs[t] : kbufs[t]);
+  wait_vmcnt<4 * T::LOADS>();  // tile 0 has landed
   // The Q loads were issued before the tile loads, so they are complete now;
   // a use here settles the compiler's load tracking for those registers once,
   // instead of a full wait for all loads at their first use inside the loop.
@@ -445,19 +432,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   block_barrier();
   if (grp == 1) block_barrier();
   if (active(0)) matrix(vb(0), kb(0), false, true);
-  if (grp == 1) wait_batches(batch_tiles(-2) + batch_tiles(-1));
+  wait_vmcnt<2 * T::LOADS>();  // tile 1
   block_barrier();
 
   auto iter = [&](int j, auto phase, auto clean) __attribute__((always_inline)) {
     constexpr int P = decltype(phase)::value;  // j mod 4
     constexpr bool CLEAN = decltype(clean)::value;
-    // Y(j)
-    if (grp == 1) issue_batch(j, phase);
+    // Y(j), with this group's tile j+3
+    load_tile(j + 3, grp ? vbufs[(P + 3) & 3] : kbufs[(P + 3) & 3]);
     if (CLEAN)
       softmax(j, std::true_type{});
     else if (active(j))
       softmax(j, std::false_type{});
-    if (grp == 1) wait_batches(batch_tiles(j - 1) + batch_tiles(j));
+    wait_vmcnt<4 * T::LOADS>();  // tile j+1
     block_barrier();
     // X(j)
     if (CLEAN)
@@ -494,8 +481,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
   // O leaves the accumulators as 8-byte pieces of 32 different rows per
   // instruction; written to HBM like that, each row segment is a separate
   // partial-line write.  The wavefront stages its 32 rows in LDS instead (a K
-  // or V buffer: every wavefront is past its last read of them) and writes
-  // them back as whole rows, 16 bytes a lane.
+  // or V buffer: every wavefront is past its last read of them and every load
+  // has landed) and writes them back as whole rows, 16 bytes a lane.
+  wait_vmcnt<0>();  // the loads past the last tile write tile buffers too
+  block_barrier();
   l = pair_sum(l);
   const float lbs = pair_sum(lb[0] + lb[1]);
   const float inv = (SPARSE && lbs == 0.f) ? 0.f : 1.f / lbs;  // SPARSE: a row with no key writes O = 0, L = −∞
