@@ -29,6 +29,7 @@ from .ref import (
     decode_paged_ref,
     attention_bwd_ref,
     attention_block_sparse_ref,
+    masked_probs,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode, bwd_allowance, check_bwd
 
@@ -41,6 +42,7 @@ __all__ = [
     "decode_paged_ref",
     "attention_bwd_ref",
     "attention_block_sparse_ref",
+    "masked_probs",
     "bf16_half_ulp",
     "o_excess",
     "check_prefill",

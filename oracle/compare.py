@@ -77,7 +77,7 @@ U_BF16 = 2.0 ** -8   # unit roundoff of round-to-nearest bf16 (8 significant bit
 U_F32 = 2.0 ** -24
 
 
-def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False):
+def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False, block_mask=None, block=128):
     """Per-element error allowance of a bf16-operand, fp32-accumulating backward.
 
     Reference values are those of ``attention_bwd_ref`` (same arguments).  The
@@ -91,6 +91,8 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False):
         |ΔdV| ≤ (u_P + γ_N)·Pᵀ|dO|
         |ΔdK| ≤ scale·(|ΔdS|ᵀ|Q| + γ_N·|dS|ᵀ|Q|),   |ΔdQ| likewise with |K|
     with γ_n = n·2^-24 (fp32 sums of n terms).
+    ``block_mask``/``block``: the block-sparse backward (P of switched-off
+    blocks and of rows without keys is zero; the same bounds hold term by term).
     ``o_from_fwd``: the kernel's O and L come from a forward of the same
     arithmetic (weights P̃ rounded to bf16 in both the sum Σ P̃ v and its
     normaliser, fp32 sums) while the reference uses the exact O; then
@@ -100,12 +102,14 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False):
     Returns ((dq, dk, dv) reference, (dq, dk, dv) allowance), all float64;
     the output rounding to bf16 is added by ``check_bwd``.
     """
-    from .ref import as_f64, attention_ref, safe_softmax, scores, attention_bwd_ref
+    from .ref import as_f64, attention_ref, attention_block_sparse_ref, masked_probs, attention_bwd_ref
 
-    dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal, o=o)
+    dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal, o=o, block_mask=block_mask, block=block)
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    mask = None if block_mask is None else np.asarray(block_mask)
     if o is None:
-        o, _ = attention_ref(q, k, v, scale, causal)
+        o = (attention_ref(q, k, v, scale, causal) if mask is None
+             else attention_block_sparse_ref(q, k, v, scale, causal, mask, block))[0]
     o = as_f64(o)
     B, H, N, d = q.shape
     g_d, g_n = d * U_F32, N * U_F32
@@ -113,7 +117,8 @@ def bwd_allowance(q, k, v, do, scale, causal, o=None, o_from_fwd=False):
     aq, ak, av = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
         for h in range(H):
-            p, _, _ = safe_softmax(scores(q[b, h], k[b, h], scale, causal))
+            mk = None if mask is None else (mask if mask.ndim == 2 else mask[b * H + h])
+            p = masked_probs(q[b, h], k[b, h], scale, causal, mk, block)
             ado = np.abs(do[b, h])
             dp = do[b, h] @ v[b, h].T
             dd = (do[b, h] * o[b, h]).sum(axis=1)

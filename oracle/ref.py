@@ -225,7 +225,25 @@ def attention_block_sparse_ref(q, k, v, scale, causal, block_mask, block=128, ro
     return o, lse
 
 
-def attention_bwd_ref(q, k, v, do, scale, causal, o=None):
+def masked_probs(q_bh, k_bh, scale, causal, block_mask_bh=None, block=128):
+    """The softmax weights P of one (b, h): P = softmax(S) row by row, S the
+    scaled scores with the causal mask and, when ``block_mask_bh`` ([T_q, T_k]
+    of 0/1) is given, the switched-off blocks at −∞ ([FA-1拆解] "块稀疏扩展").
+    A row with no key left has no softmax; its weights are taken as all zero,
+    matching O = 0 for that row."""
+    s = scores(q_bh, k_bh, scale, causal)
+    if block_mask_bh is None:
+        p, _, _ = safe_softmax(s)
+        return p
+    n = s.shape[0]
+    idx = np.arange(n) // block
+    s = np.where(np.asarray(block_mask_bh)[idx[:, None], idx[None, :]] != 0, s, -np.inf)
+    empty = np.all(np.isneginf(s), axis=1)
+    p, _, _ = safe_softmax(np.where(empty[:, None], 0.0, s))
+    return np.where(empty[:, None], 0.0, p)
+
+
+def attention_bwd_ref(q, k, v, do, scale, causal, o=None, block_mask=None, block=128):
     """Exact attention backward: the gradients of Σ dO ∘ O with respect to Q, K, V.
 
     The chain rule through O = P V and the row softmax P = softmax(S),
@@ -238,6 +256,10 @@ def attention_bwd_ref(q, k, v, do, scale, causal, o=None):
     D_i = Σ_c dO_ic O_ic, the identity of [15-779 L5] §7.3 that lets a
     blockwise backward form D before its loops; it equals Σ_j P_ij dP_ij when
     o is the exact O.
+    ``block_mask`` ([T_q, T_k] or [B·H, T_q, T_k], as for
+    ``attention_block_sparse_ref``): the backward of block-sparse attention;
+    switched-off blocks have P = 0 and so dS = 0, and a row with no key has
+    P = 0, O = 0 and zero gradient.
     q, k, v, do: [B, H, N, d].  Returns (dQ, dK, dV, D) as float64 arrays,
     D of shape [B, H, N].
     """
@@ -246,12 +268,14 @@ def attention_bwd_ref(q, k, v, do, scale, causal, o=None):
     v = as_f64(v)
     do = as_f64(do)
     o = None if o is None else as_f64(o)
+    mask = None if block_mask is None else np.asarray(block_mask)
     B, H, N, _ = q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     dd = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            p, _, _ = safe_softmax(scores(q[b, h], k[b, h], scale, causal))
+            mk = None if mask is None else (mask if mask.ndim == 2 else mask[b * H + h])
+            p = masked_probs(q[b, h], k[b, h], scale, causal, mk, block)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
             dd[b, h] = (p * dp).sum(axis=1) if o is None else (do[b, h] * o[b, h]).sum(axis=1)

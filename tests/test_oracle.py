@@ -461,6 +461,58 @@ def test_backward_dv_with_constant_do_is_column_sums():
 
 
 # --------------------------------------------------------------------------
+# backward of block-sparse attention
+
+
+def _sparse_loss(q, k, v, do, scale, causal, mask, block):
+    return float((attention_block_sparse_ref(q, k, v, scale, causal, mask, block)[0] * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_matches_central_differences(causal):
+    """With a block mask (blocks of 2 over N = 7: a partial last block, a row
+    block that keeps nothing, kept and dropped blocks mixed), dQ, dK, dV are
+    the gradients of Σ dO ∘ O through the block-sparse forward definition:
+    central differences (step 1e-5, fp64) agree to 1e-8, and the rows with no
+    key get exactly zero dQ."""
+    rng = np.random.default_rng(61 + causal)
+    B, H, N, d, blk = 1, 2, 7, 3, 2
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    mask = np.array([[1, 0, 1, 0], [0, 0, 0, 0], [1, 1, 0, 1], [0, 1, 1, 1]])
+    scale = 0.6
+    dq, dk, dv, _ = attention_bwd_ref(q, k, v, do, scale, causal, block_mask=mask, block=blk)
+    assert np.all(dq[:, :, 2:4] == 0)
+    eps = 1e-5
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            up = _sparse_loss(q, k, v, do, scale, causal, mask, blk)
+            x[idx] = keep - eps
+            down = _sparse_loss(q, k, v, do, scale, causal, mask, blk)
+            x[idx] = keep
+            num[idx] = (up - down) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-8)
+
+
+def test_block_sparse_backward_special_cases():
+    """An all-ones mask is the dense backward; a block-diagonal mask splits the
+    problem into independent attentions over the two halves."""
+    rng = np.random.default_rng(67)
+    q, k, v, do = (rng.standard_normal((1, 2, 16, 4)) for _ in range(4))
+    dense = attention_bwd_ref(q, k, v, do, 0.5, True)
+    ones = attention_bwd_ref(q, k, v, do, 0.5, True, block_mask=np.ones((2, 2)), block=8)
+    for a, b in zip(dense, ones):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-14)
+    diag = attention_bwd_ref(q, k, v, do, 0.5, False, block_mask=np.eye(2), block=8)
+    for half in (slice(0, 8), slice(8, 16)):
+        part = attention_bwd_ref(q[:, :, half], k[:, :, half], v[:, :, half], do[:, :, half], 0.5, False)
+        for a, b in zip(part[:3], diag[:3]):
+            np.testing.assert_allclose(b[:, :, half], a, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # the tolerance rule
 
 
@@ -587,9 +639,9 @@ def test_block_sparse_empty_rows_and_per_head_masks():
 # narrow enough to fail plausible slips
 
 
-def _sim_bwd(q, k, v, do, o, lse, scale, causal, slip=None):
+def _sim_bwd(q, k, v, do, o, lse, scale, causal, slip=None, mask=None, block=128):
     """A bf16-operand, fp32-accumulating backward in numpy float32 (the arithmetic
-    bwd_allowance describes), with an optional planted slip."""
+    bwd_allowance describes), with an optional planted slip and block mask."""
     f = np.float32
     c = f(scale * math.log2(math.e))
     out = [np.empty(q.shape, np.float64) for _ in range(3)]
@@ -602,6 +654,9 @@ def _sim_bwd(q, k, v, do, o, lse, scale, causal, slip=None):
             p = np.exp2(s * c - (l2[:, None] if slip != "no_lse" else f(0)))
             if causal and slip != "no_mask":
                 p[np.triu_indices(N, 1)] = 0
+            if mask is not None and slip != "no_block_mask":
+                idx = np.arange(N) // block
+                p = np.where(np.asarray(mask)[idx[:, None], idx[None, :]] != 0, p, f(0))
             dp = dd_o @ vv.T
             dvec = (dd_o * oo).sum(axis=1)
             ds = p * (dp - (dvec[:, None] if slip != "no_d" else f(0)))
@@ -653,6 +708,23 @@ def test_bwd_allowance_covers_forward_then_backward(causal):
     ref, allow = bwd_allowance(q, k, v, do, scale, causal, o_from_fwd=True)
     rep = check_bwd(_sim_bwd(q, k, v, do, o, lse, scale, causal), ref, allow)
     assert rep["pass"], rep
+
+
+@pytest.mark.parametrize("slip", [None, "no_block_mask"])
+def test_bwd_allowance_block_sparse(slip):
+    """The rule with a block mask (blocks of 16 over N = 48, one row block that
+    keeps only a far key block): the float32 simulation passes, and one that
+    forgets the block mask fails."""
+    causal = True
+    rng = np.random.default_rng(71)
+    q, k, v, do = (bf16_rne(rng.standard_normal((1, 2, 48, 16))) for _ in range(4))
+    scale = float(np.float32(0.25))
+    mask = np.array([[1, 0, 0], [0, 1, 0], [1, 0, 1]])
+    o, lse = attention_block_sparse_ref(q, k, v, scale, causal, mask, 16)
+    o, lse = bf16_rne(o), np.asarray(lse, dtype=np.float32)
+    ref, allow = bwd_allowance(q, k, v, do, scale, causal, o=o, block_mask=mask, block=16)
+    rep = check_bwd(_sim_bwd(q, k, v, do, o, lse, scale, causal, slip=slip, mask=mask, block=16), ref, allow)
+    assert rep["pass"] == (slip is None), rep
 
 
 @pytest.mark.parametrize("slip", ["no_d", "no_mask", "no_scale", "no_lse", "dv_untransposed"])
