@@ -15,6 +15,7 @@ library is missing or fails to load, the calls raise.
     fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, N)                  -> int
     fa_bwd_atomic(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+    fa_bwd_block_sparse(q, k, v, o, lse, do, block_mask, scale=None, causal=False) -> (dq, dk, dv)
     fa_bwd_atomic_workspace_bytes(B, H, N, d)        -> int
     fa_fwd_tile_pairs(N, d, causal)                  -> int   (host-only)
     fa_fwd_tile_shape(d)                             -> (block_m, block_n)
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_atomic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_atomic.restype = i
+    lib.fa_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_bwd_block_sparse.restype = i
     lib.fa_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_atomic_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, f, i, vp, sz, vp]
@@ -172,6 +175,23 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
 SPARSE_BLOCK = 128
 
 
+def _check_mask(block_mask, BH, T, device):
+    """The block mask as a contiguous uint8 [1 or B·H, T, T] tensor on ``device``."""
+    torch = _torch()
+    m = block_mask
+    if not isinstance(m, torch.Tensor) or m.device != device:
+        raise ValueError("block_mask must be a tensor on q's device")
+    if m.dtype == torch.bool:
+        m = m.to(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise TypeError("block_mask must be uint8 or bool")
+    if m.dim() == 2:
+        m = m.unsqueeze(0)
+    if m.dim() != 3 or m.shape[1:] != (T, T) or m.shape[0] not in (1, BH):
+        raise ValueError(f"block_mask must be [T, T] or [B*H, T, T] with T = {T}, got {tuple(block_mask.shape)}")
+    return m.contiguous()
+
+
 def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None):
     """Block-sparse prefill: fa_fwd with the score blocks whose mask entry is zero set
     to −∞ and skipped.  ``block_mask``: uint8 (or bool) [T, T] or [B·H, T, T] on q's
@@ -183,18 +203,7 @@ def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None,
         raise ValueError("q, k, v shapes differ")
     B, H, N, d = q.shape
     T = -(-N // SPARSE_BLOCK)
-    m = block_mask
-    if not isinstance(m, torch.Tensor) or m.device != q.device:
-        raise ValueError("block_mask must be a tensor on q's device")
-    if m.dtype == torch.bool:
-        m = m.to(torch.uint8)
-    if m.dtype != torch.uint8:
-        raise TypeError("block_mask must be uint8 or bool")
-    if m.dim() == 2:
-        m = m.unsqueeze(0)
-    if m.dim() != 3 or m.shape[1:] != (T, T) or m.shape[0] not in (1, B * H):
-        raise ValueError(f"block_mask must be [T, T] or [B*H, T, T] with T = {T}, got {tuple(block_mask.shape)}")
-    m = m.contiguous()
+    m = _check_mask(block_mask, B * H, T, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -298,7 +307,7 @@ def fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None, workspace=
     return o, lse
 
 
-def _bwd_call(fn, q, k, v, o, lse, do, scale, causal, workspace):
+def _bwd_call(fn, q, k, v, o, lse, do, scale, causal, workspace, block_mask=None):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check(t, n, 4)
@@ -316,10 +325,12 @@ def _bwd_call(fn, q, k, v, o, lse, do, scale, causal, workspace):
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = getattr(load_library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                                     float(scale), int(bool(causal)), workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal))]
+    if block_mask is not None:
+        args += [block_mask.data_ptr(), block_mask.shape[0]]
+    st = getattr(load_library(), fn)(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, fn)
     return dq, dk, dv
@@ -334,6 +345,17 @@ def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
     torch when not given.  Runs on the current stream.  Deterministic.
     """
     return _bwd_call("fa_bwd", q, k, v, o, lse, do, scale, causal, workspace)
+
+
+def fa_bwd_block_sparse(q, k, v, o, lse, do, block_mask, scale=None, causal=False, workspace=None):
+    """Backward of fa_fwd_block_sparse: as fa_bwd, with the block mask the forward
+    used (uint8 [T, T] or [B·H, T, T], T = ⌈N/128⌉, on the device).  o and lse
+    must be that forward's outputs."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    T = -(-N // SPARSE_BLOCK)
+    m = _check_mask(block_mask, B * H, T, q.device)
+    return _bwd_call("fa_bwd_block_sparse", q, k, v, o, lse, do, scale, causal, workspace, block_mask=m)
 
 
 def fa_bwd_atomic(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):

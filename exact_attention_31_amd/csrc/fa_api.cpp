@@ -147,7 +147,7 @@ size_t dqacc_offset(size_t ld_bytes) { return (ld_bytes + 255) & ~(size_t)255; }
 
 fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                    void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
-                   size_t workspace_bytes, bool fused, void* stream) {
+                   size_t workspace_bytes, bool fused, const unsigned char* block_mask, int mask_heads, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -172,6 +172,14 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
     for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
   }
+  const int nb = fa::ceil_div(N, fa::kSparseBlock);
+  if (block_mask) {
+    if (nb > fa::kSparseMaxBlocks) return FA_ERR_SHAPE;
+    if (mask_heads != 1 && mask_heads != B * H) return FA_ERR_SHAPE;
+    const size_t mb = (size_t)mask_heads * nb * nb;
+    for (int a = 0; a < 4; ++a)
+      if (overlap(outs[a], out_bytes[a], block_mask, mb)) return FA_ERR_ALIAS;
+  }
 
   fa::BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -186,6 +194,9 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.ld = static_cast<float*>(workspace);
   p.dqacc = fused ? reinterpret_cast<float*>(static_cast<char*>(workspace) + dqacc_offset(fa_bwd_workspace_bytes(B, H, N)))
                   : nullptr;
+  p.block_mask = block_mask;
+  p.mask_heads = mask_heads;
+  p.mask_t = nb;
   p.BH = B * H;
   p.N = N;
   p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
@@ -213,14 +224,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
                  size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes, false,
-                  stream);
+                  nullptr, 0, stream);
 }
 
 fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                         void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                         void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes, true,
-                  stream);
+                  nullptr, 0, stream);
+}
+
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, const unsigned char* block_mask, int mask_heads, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!block_mask) return FA_ERR_NULL;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes, false,
+                  block_mask, mask_heads, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {

@@ -246,8 +246,13 @@ __device__ inline void decode_kblock(const BwdParams& p, int& bh, int& kb) {
 // through LDS ([key][query] bf16), the next step multiplies it by the block's
 // K tile (kept in LDS) and adds the block's share of dQ to an fp32 buffer with
 // atomic adds.  Every wait then covers all outstanding memory operations.
-template <int D, bool CAUSAL, bool FUSED>
+// SPARSE: the backward of block-sparse attention; the workgroup lists the
+// query blocks (kSparseBlock rows) whose mask keeps its key block and steps
+// through those only.
+template <int D, bool CAUSAL, bool FUSED, bool SPARSE>
 __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(!(FUSED && SPARSE), "the block-sparse backward takes the two-pass form");
+  static_assert(kBwdBlockK == kSparseBlock, "one key block is one mask block");
   using T = BwdTile<D>;
   using TS = BwdTile<64>;  // the dS tile: 64 query columns (128-byte rows) per key
   constexpr int W = kBwdKvWaves;
@@ -319,7 +324,37 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   }
 
   const int first = CAUSAL ? k0 / BM : 0;  // query tiles before the block's first key see none of it
-  const int n_steps = ceil_div(N, BM) - first;
+  // SPARSE: the kept query blocks in ascending order (causal: from the key
+  // block's own on), compacted by wavefront 0 with a ballot over the mask column
+  __shared__ uint16_t qblocks[SPARSE ? kSparseMaxBlocks : 1];
+  int n_steps;
+  if constexpr (SPARSE) {
+    const uint8_t* col = p.block_mask + (size_t)(p.mask_heads == 1 ? 0 : bh) * p.mask_t * p.mask_t + kb;
+    int count = 0;
+    if (wave_u == 0) {
+      for (int b0 = CAUSAL ? kb : 0; b0 < p.mask_t; b0 += 64) {
+        const int qbk = b0 + lane;
+        const int keep = qbk < p.mask_t ? (col[(size_t)qbk * p.mask_t] != 0) : 0;
+        const uint64_t bal = __ballot(keep);
+        const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (keep) qblocks[pos] = (uint16_t)qbk;
+        count += __popcll(bal);
+      }
+    }
+    __shared__ int qblock_count;
+    if (threadIdx.x == 0) qblock_count = count;
+    __syncthreads();
+    n_steps = 2 * __builtin_amdgcn_readfirstlane(qblock_count);
+  } else {
+    n_steps = ceil_div(N, BM) - first;
+  }
+  // first query row of step s; at or past N for the steps past the last
+  auto step_row = [&](int s) __attribute__((always_inline)) {
+    if constexpr (SPARSE)
+      return s < n_steps ? (int)__builtin_amdgcn_readfirstlane(qblocks[s >> 1]) * kSparseBlock + (s & 1) * BM : N;
+    else
+      return (first + s) * BM;
+  };
   // Stage loads: wavefront w issues loads w, w + W, ... of the 2R runs (Q
   // runs first, then dO); the lane's offset is the same for all of them.
   const int x0 = wave_u % R;
@@ -329,8 +364,8 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   // keeps the same number of loads in flight.
   auto issue_tile = [&](int s, auto buf, int i) __attribute__((always_inline)) {  // load i < PER of stage s
     constexpr int B = decltype(buf)::value;
-    const int toff = (first + s) * QT;  // byte offset of the stage's first row
-    const int x = wave_u + i * W;       // i < R / W exactly when x < R (W divides R)
+    const int toff = step_row(s) * T::ROW;  // byte offset of the stage's first row
+    const int x = wave_u + i * W;           // i < R / W exactly when x < R (W divides R)
     if (i * W < R)
       load_lds16(qrsrc, qbufs[B] + x * 1024, goff + toff + (x - x0) * 1024);
     else
@@ -338,8 +373,8 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   };
   auto issue_ld = [&](int s, auto buf) __attribute__((always_inline)) {  // the stage's (L, D) pairs
     constexpr int B = decltype(buf)::value;
-    if (wave_u == 0) load_lds4(lrsrc, lbufs[B], lane * 4 + (first + s) * BM * 8);
-    if (wave_u == 1) load_lds4(lrsrc, lbufs[B] + 64, lane * 4 + (first + s) * BM * 8 + 256);
+    if (wave_u == 0) load_lds4(lrsrc, lbufs[B], lane * 4 + step_row(s) * 8);
+    if (wave_u == 1) load_lds4(lrsrc, lbufs[B] + 64, lane * 4 + step_row(s) * 8 + 256);
   };
   auto issue = [&](int s, auto buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -500,7 +535,7 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
         a2[iu] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TileReads<64>::tr_at(ds_lds, dso0[iu], dso8[iu], kk), kb8,
                                                          a2[iu], 0, 0, 0);
     }
-    const int qs = (first + s_prev) * BM;
+    const int qs = step_row(s_prev);
     float* dst = p.dqacc + ((size_t)bh * N) * D + dq_ds * 32 + i32;
 #pragma unroll
     for (int iu = 0; iu < DQ_NU; ++iu)
@@ -513,7 +548,7 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   // CLEAN: every query of the step comes at or after every key of the block.
   auto step = [&](int s, auto buf, auto clean) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
-    const int qs0 = (first + s) * BM;
+    const int qs0 = step_row(s);
     auto issue_next = [&](int i) __attribute__((always_inline)) {
       issue_tile(s + 2, std::integral_constant<int, (B + 2) % 3>{}, i);
     };
@@ -575,10 +610,16 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
     // The block's keys are 128 from a multiple of 128, its steps 64 queries
     // from the first key on: the first two steps hold the diagonal (masked),
     // and from the third on every query follows every key of the block.
+    // SPARSE: so when the diagonal block is kept (it is then the first);
+    // otherwise every listed query follows every key of the block.
     static_assert(kBwdBlockK == 2 * BM, "two diagonal steps");
-    body(0, I0{}, G{});
-    if (n_steps > 1) body(1, I1{}, G{});
-    loop(2, I2{});
+    if (!SPARSE || (n_steps > 0 && step_row(0) == k0)) {
+      body(0, I0{}, G{});
+      if (n_steps > 1) body(1, I1{}, G{});
+      loop(2, I2{});
+    } else {
+      loop(0, I0{});
+    }
   } else {
     loop(0, I0{});
   }
@@ -620,7 +661,10 @@ __device__ inline void decode_qblock(const BwdParams& p, int& bh, int& qb) {
   }
 }
 
-template <int D, bool CAUSAL>
+// SPARSE: the workgroup's 256 rows span two mask rows; it lists the key
+// blocks either of them keeps (as the block-sparse forward does) and each
+// wavefront skips the tiles its own mask row drops.
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int BN = 64;              // keys per tile
@@ -663,14 +707,55 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   TileReads<D> rd;
   rd.init(lane);
 
-  const int n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
+  // SPARSE: kept key blocks, bits 0-13 the block, bit 14 (15) set when the
+  // first (second) mask row of the workgroup keeps it
+  __shared__ uint16_t kblocks[SPARSE ? kSparseMaxBlocks : 1];
+  int n_tiles;
+  if constexpr (SPARSE) {
+    static_assert(kSparseBlock == 2 * BN && kFwdBlockM == 2 * kSparseBlock, "two tiles per key block, two mask rows");
+    const int rb0 = q0 / kSparseBlock;
+    const bool two = rb0 + 1 < p.mask_t;
+    const uint8_t* m0 = p.block_mask + ((size_t)(p.mask_heads == 1 ? 0 : bh) * p.mask_t + rb0) * p.mask_t;
+    const int kb_end = CAUSAL ? min(p.mask_t, ceil_div(min(N, q0 + kFwdBlockM), kSparseBlock)) : p.mask_t;
+    int count = 0;
+    if (wave_u == 0) {
+      for (int b0 = 0; b0 < kb_end; b0 += 64) {
+        const int kbk = b0 + lane;
+        const int k0b = kbk < kb_end ? (m0[kbk] != 0) : 0;
+        const int k1b = (kbk < kb_end && two) ? (m0[p.mask_t + kbk] != 0) : 0;
+        const uint64_t bal = __ballot(k0b | k1b);
+        const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (k0b | k1b) kblocks[pos] = (uint16_t)(kbk | (k0b << 14) | (k1b << 15));
+        count += __popcll(bal);
+      }
+    }
+    __shared__ int kblock_count;
+    if (threadIdx.x == 0) kblock_count = count;
+    __syncthreads();
+    n_tiles = 2 * __builtin_amdgcn_readfirstlane(kblock_count);
+  } else {
+    n_tiles = fwd_kv_tiles(N, D, CAUSAL, qb);
+  }
+  // first key of tile j (SPARSE: of the j-th tile of the kept blocks)
+  auto tile_kv0 = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE)
+      return (int)(__builtin_amdgcn_readfirstlane(kblocks[j >> 1]) & 0x3fff) * kSparseBlock + (j & 1) * BN;
+    else
+      return j * BN;
+  };
+  auto kept = [&](int j) __attribute__((always_inline)) {  // SPARSE: this wavefront's mask row keeps tile j
+    if constexpr (SPARSE)
+      return ((__builtin_amdgcn_readfirstlane(kblocks[j >> 1]) >> (14 + (wave_u >> 2))) & 1) != 0;
+    else
+      return true;
+  };
   const int goff = run_goff<D>(wave_u % R, lane);
   // Tiles past the last are loaded all the same, from past the end of K and V
   // (zeros, no memory traffic) into a buffer nobody reads again, and every
   // step then keeps the same number of loads in flight.
   auto issue_tile = [&](int j, auto buf, int i) __attribute__((always_inline)) {  // load i < PER of tile j
     constexpr int B = decltype(buf)::value;
-    const int toff = j < n_tiles ? j * KT : N * T::ROW;  // byte offset of the tile's first row
+    const int toff = j < n_tiles ? tile_kv0(j) * T::ROW : N * T::ROW;  // byte offset of the tile's first row
     const int x = wave_u + i * kFwdWaves;  // i < R / 8 exactly when x < R (8 divides R)
     if (i * kFwdWaves < R)
       load_lds16(krsrc, kbufs[B] + x * 1024, goff + toff + (x - wave_u % R) * 1024);
@@ -699,11 +784,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
     auto issue_next = [&](int i) __attribute__((always_inline)) {
       issue_tile(j + 2, std::integral_constant<int, (B + 2) % 3>{}, i);
     };
-    const int kv0 = j * BN;
+    const int kv0 = tile_kv0(j);
     if (!CLEAN) {  // tiles with a mask or a skip: the loads go out first
 #pragma unroll
       for (int i = 0; i < PER; ++i) issue_next(i);
       if (CAUSAL && kv0 > wq0 + 31) return;  // the tile lies wholly after this wavefront's rows
+      if (!kept(j)) return;                  // SPARSE: this wavefront's mask row drops it
     }
     const unsigned char* kb = kbufs[B];
     const unsigned char* vb = vbufs[B];
@@ -799,7 +885,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
   using Y = std::true_type;
   using G = std::false_type;
   // tiles 0 .. n_clean-1 are whole and before the diagonal of every row of the block
-  const int n_clean = CAUSAL ? min(N / BN, (q0 + 1) / BN) : N / BN;
+  const int n_clean = SPARSE ? 0 : CAUSAL ? min(N / BN, (q0 + 1) / BN) : N / BN;
   int j = 0;
   for (; j + 3 <= n_clean; j += 3) {
     body(j, I0{}, Y{});
@@ -835,20 +921,30 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.block_mask) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, false, true>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
+                       stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, true>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.dqacc) {
-    static const hipError_t attr = allow_full_lds(&fa_bwd_dkdv_kernel<D, CAUSAL, true>);
+    static const hipError_t attr = allow_full_lds(&fa_bwd_dkdv_kernel<D, CAUSAL, true, false>);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, true>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, true, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
+                       stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long n8 = rows * D / 8;
     hipLaunchKernelGGL((fa_bwd_dq_finish_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, false, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
+                     stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

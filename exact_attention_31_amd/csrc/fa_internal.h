@@ -84,6 +84,9 @@ struct BwdParams {
   uint16_t* dv;
   float* ld;         // workspace [BH, N] pairs (L·log2 e, D = dO·O)
   float* dqacc;      // null: dQ by its own pass; else workspace fp32 [BH, N, d] for atomic adds
+  const uint8_t* block_mask;  // null: dense; else [mask_heads, mask_t, mask_t] of kSparseBlock blocks
+  int mask_heads;    // 1 or BH
+  int mask_t;        // ceil(N / kSparseBlock)
   int BH;
   int N;
   int n_qblk;        // query blocks of kFwdBlockM rows (dQ kernel)

@@ -25,7 +25,8 @@
  *              the probabilities recomputed rather than stored
  *              ([15-779 L5] §7; [pinghaoyang FA-1] "Backward").
  *   fa_bwd_atomic  the same gradients in one key-block pass with dQ added up
- *              atomically ([15-779 L5] §7.4): faster, not bit-reproducible.
+ *              atomically ([15-779 L5] §7.4): not bit-reproducible.
+ *   fa_bwd_block_sparse  backward of fa_fwd_block_sparse.
  *
  * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
  * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
@@ -153,6 +154,22 @@ size_t fa_bwd_atomic_workspace_bytes(int B, int H, int N, int d);
 fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                         float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of fa_fwd_block_sparse ([FA-1拆解] "块稀疏扩展" applied to the
+ * backward of [15-779 L5] §7): the gradients of the loss through
+ * O = fa_fwd_block_sparse(q, k, v, block_mask).  Switched-off blocks of the
+ * score matrix contribute nothing and their tiles are skipped in both passes
+ * (the dK/dV pass walks only the query blocks that keep its key block, the dQ
+ * pass only the key blocks its rows keep).  Arguments, layouts, workspace
+ * (fa_bwd_workspace_bytes) and errors as for fa_bwd; block_mask and
+ * mask_heads as for fa_fwd_block_sparse, and o and lse must be that call's
+ * outputs (a row with no key has O = 0, L = −∞ and gets dQ = 0).  FA_ERR_NULL
+ * for a missing mask, FA_ERR_ALIAS when an output or the workspace overlaps
+ * the mask.  Deterministic. */
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                              float scale, int causal, const unsigned char* block_mask, int mask_heads,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fa_decode needs for these sizes: the per-split
  * partial results, fp32 [B, H, num_splits, d] then fp32 [B, H, num_splits].

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("fa_fwd", "fa_decode", "fa_decode_gqa", "fa_decode_workspace_bytes", "fa_status_str",
                  "fa_fwd_tile_pairs", "fa_fwd_tile_shape", "fa_abi_version", "fa_bwd", "fa_bwd_workspace_bytes",
-                 "fa_fwd_block_sparse", "fa_decode_paged", "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes"):
+                 "fa_fwd_block_sparse", "fa_decode_paged", "fa_bwd_atomic", "fa_bwd_atomic_workspace_bytes",
+                 "fa_bwd_block_sparse"):
         assert want in names
 
 
@@ -172,6 +173,25 @@ def test_bwd_atomic_argument_checks():
     assert _bwda(ws=MISALIGNED) == 4
     assert _lib().fa_bwd_atomic_workspace_bytes(1, 1, 1, 80) == 0
     assert _lib().fa_bwd_atomic_workspace_bytes(0, 1, 1, 64) == 0
+
+
+def _bwds(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, N=300, d=64,
+          scale=0.125, causal=1, mask=ctypes.c_void_p(0xC0000000), mh=1, ws=P[9], wsb=1 << 20):
+    return _lib().fa_bwd_block_sparse(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, ctypes.c_float(scale), causal,
+                                      mask, mh, ws, wsb, None)
+
+
+def test_bwd_block_sparse_argument_checks():
+    """fa_bwd's checks plus the mask's (as for fa_fwd_block_sparse)."""
+    assert _bwds(mask=None) == 1 and _bwds(dq=None) == 1
+    assert _bwds(mh=3) == 2 and _bwds(mh=0) == 2          # one mask, or one per (b, h) = 2
+    assert _bwds(N=1024 * 128 + 1, wsb=1 << 30) == 2     # more than 1024 key blocks
+    assert _bwds(d=80) == 3 and _bwds(scale=0.0) == 5
+    assert _bwds(ws=None) == 6 and _bwds(wsb=2 * 300 * 8 - 1) == 6
+    assert _bwds(dv=MISALIGNED) == 4
+    assert _bwds(dq=ctypes.c_void_p(0xC0000000 - 1024)) == 8  # dQ running into the mask
+    assert _bwds(ws=ctypes.c_void_p(0xC0000000 - 4096)) == 8  # workspace running into the mask
+    assert _bwds(dk=P[0]) == 8
 
 
 def _paged(q=P[0], kp=P[1], vp=P[2], o=P[3], lse=P[4], B=2, Hq=4, Hkv=2, d=64, ps=16, npg=8, tbl=P[5], mp=4,

@@ -2,7 +2,10 @@
 against the fp64 oracle (attention_block_sparse_ref), same rule as the dense
 forward (oracle/compare.py), plus exact agreement with fa_fwd where the mask
 keeps everything the dense call computes.  Rows the mask leaves without keys
-must come back as O = 0 and LSE = −∞."""
+must come back as O = 0 and LSE = −∞.  The backward (fa_bwd_block_sparse),
+fed the block-sparse forward's own O and L, is checked against the oracle's
+backward with the same mask under bwd_allowance (oracle/compare.py), and is bit
+for bit fa_bwd where the mask keeps everything the dense call computes."""
 
 import sys
 
@@ -13,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 import exact_attention_31_amd as fa
 import synth
-from oracle import attention_block_sparse_ref, check_prefill
+from oracle import attention_block_sparse_ref, bwd_allowance, check_bwd, check_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +104,71 @@ def test_block_sparse_long_sampled_rows():
                                         rows=rows)
     _check("long N16384 (sampled)", o[:, heads][:, :, rows].float().cpu().numpy(),
            lse[:, heads][:, :, rows].cpu().numpy(), ro, rl)
+
+
+def _bwd_check(name, got, ref, allow):
+    rep = check_bwd(got, ref, allow)
+    _say(f"[parity-sparse-bwd] {name}: " + " ".join(
+        f"{g} max_abs={rep[g + '_max_abs']:.3g} ratio={rep[g + '_ratio']:.3f}" for g in ("dq", "dk", "dv"))
+        + f" pass={rep['pass']}")
+    assert rep["pass"], rep
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,density,per_head", [(100, 0.0, False), (129, 0.5, True), (300, 0.4, False),
+                                                (513, 0.3, True), (700, 0.6, False)])
+def test_block_sparse_backward_against_oracle(n, density, per_head, causal, d):
+    """fa_fwd_block_sparse then fa_bwd_block_sparse on ragged sizes and random
+    masks (rows without keys included) against the oracle's block-sparse backward."""
+    w = W[1].with_(B=1, H=2, N=n, d=d, causal=causal, wid=150 + d // 64 + 4 * causal)
+    _say("[case] block sparse backward", n, density, per_head, causal, d)
+    q, k, v = synth.make_prefill(w)
+    do = synth.make_prefill_grad(w)
+    T = -(-n // 128)
+    mask = _random_mask(T, w.B * w.H if per_head else 1, density, 7 * n + d + causal)
+    qc, kc, vc, mc = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    o, lse = fa.fa_fwd_block_sparse(qc, kc, vc, mc, scale=w.scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd_block_sparse(qc, kc, vc, o, lse, do.cuda(), mc, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    got = [x.float().cpu().numpy() for x in (dq, dk, dv)]
+    m = mask.numpy() if per_head else mask[0].numpy()
+    ref, allow = bwd_allowance(q, k, v, do, w.scale, causal, o_from_fwd=True, block_mask=m)
+    _bwd_check(f"N={n} density={density} per_head={per_head} causal={causal} d={d}", got, ref, allow)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_sparse_backward_keeping_everything_is_the_dense_backward(d):
+    """All ones (and, with causal, the lower block triangle): fa_bwd's bits."""
+    w = W[2].with_(B=1, H=3, N=1100, d=d, boost_frac=0.01, wid=160 + d // 64)
+    _say("[case] block sparse backward vs dense", d)
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    do = synth.make_prefill_grad(w).cuda()
+    T = -(-w.N // 128)
+    for causal, mask in ((False, torch.ones(T, T, dtype=torch.uint8)),
+                         (True, torch.tril(torch.ones(T, T, dtype=torch.uint8)))):
+        o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=causal)
+        a = fa.fa_bwd(q, k, v, o, lse, do, scale=w.scale, causal=causal)
+        b = fa.fa_bwd_block_sparse(q, k, v, o, lse, do, mask.cuda(), scale=w.scale, causal=causal)
+        torch.cuda.synchronize()
+        for x, y, name in zip(a, b, ("dq", "dk", "dv")):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (causal, name)
+
+
+def test_block_sparse_backward_bench_mask_4096():
+    """B1 H4 N4096 d128 with the bench's mask recipe (own + first key block +
+    10 % random), non-causal: two heads checked against the oracle."""
+    w = W[3].with_(H=4, N=4096, wid=170)
+    _say("[case] block sparse backward 4096")
+    q, k, v = synth.make_prefill(w)
+    do = synth.make_prefill_grad(w)
+    mask = synth.make_block_mask(w, 0.1)
+    qc, kc, vc, mc = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    o, lse = fa.fa_fwd_block_sparse(qc, kc, vc, mc, scale=w.scale, causal=False)
+    dq, dk, dv = fa.fa_bwd_block_sparse(qc, kc, vc, o, lse, do.cuda(), mc, scale=w.scale, causal=False)
+    torch.cuda.synchronize()
+    hs = [0, 3]
+    got = [x[:, hs].float().cpu().numpy() for x in (dq, dk, dv)]
+    ref, allow = bwd_allowance(q[:, hs], k[:, hs], v[:, hs], do[:, hs], w.scale, False, o_from_fwd=True,
+                               block_mask=mask[0].numpy())
+    _bwd_check("B1 H4 N4096 d128 bench mask, heads [0, 3]", got, ref, allow)
