@@ -281,11 +281,37 @@ def time_sparse(torch, fa, synth, dev, args, traffic):
     flops = synth.block_sparse_flops(ws_, mask)
     kept = float(mask.float().mean())
     tf = flops / (sp * 1e-3) / 1e12
-    return {"workload": ws_.name + "_blocksparse", "mask": "own + first key block, 10 % of the rest (seeded)",
-            "kept_blocks": round(kept, 4), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(sp, 4),
-            "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "dense_ms": round(dn, 4),
-            "speedup_vs_dense": round(dn / sp, 2), "ideal_speedup": round(1 / kept, 2), "algorithmic_flops": flops,
-            "traffic": traffic_bytes(traffic, "sparse")}
+    res = {"workload": ws_.name + "_blocksparse", "mask": "own + first key block, 10 % of the rest (seeded)",
+           "kept_blocks": round(kept, 4), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(sp, 4),
+           "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "dense_ms": round(dn, 4),
+           "speedup_vs_dense": round(dn / sp, 2), "ideal_speedup": round(1 / kept, 2), "algorithmic_flops": flops,
+           "traffic": traffic_bytes(traffic, "sparse")}
+    if args.only == "sparse" and args.no_bwd_atomic:  # counter runs: the forward alone
+        return res
+    # the backward of both, on the forwards' own O and L and a seeded dO
+    do = synth.make_prefill_grad(ws_).to(dev)
+    o_s, lse_s = fa.fa_fwd_block_sparse(q, k, v, md, scale=ws_.scale)
+    o_d, lse_d = fa.fa_fwd(q, k, v, scale=ws_.scale)
+    wsp = torch.empty(fa.fa_bwd_workspace_bytes(ws_.B, ws_.H, ws_.N), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        fa.fa_bwd_block_sparse(q, k, v, o_s, lse_s, do, md, scale=ws_.scale, workspace=wsp)
+        fa.fa_bwd(q, k, v, o_d, lse_d, do, scale=ws_.scale, workspace=wsp)
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        fa.fa_bwd_block_sparse(q, k, v, o_s, lse_s, do, md, scale=ws_.scale, workspace=wsp)
+        e[1].record()
+        e[2].record()
+        fa.fa_bwd(q, k, v, o_d, lse_d, do, scale=ws_.scale, workspace=wsp)
+        e[3].record()
+    torch.cuda.synchronize()
+    bsp = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    bdn = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev)
+    bflops = 2.5 * flops  # the five products of the backward against the forward's two
+    res["backward"] = {"value": round(bflops / (bsp * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms": round(bsp, 4),
+                       "dense_ms": round(bdn, 4), "speedup_vs_dense": round(bdn / bsp, 2),
+                       "note": "fa_bwd_block_sparse against fa_bwd on the same workload; five products of the kept blocks"}
+    return res
 
 
 def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
