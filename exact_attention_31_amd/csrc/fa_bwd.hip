@@ -806,7 +806,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
     // sub-tile 0; C: dQ of sub-tile 0's keys with that of sub-tile 1; D: the rest
     constexpr int NA = 2 * T::KS;      // MFMAs of S and dP per 32-key sub-tile
     constexpr int NC = 2 * T::DSUB;    // dQ MFMAs per 32 keys (two k-steps)
-    constexpr int LA = 4, LC = 2;
+    constexpr int LA = SPARSE ? 3 : 4, LC = 2;  // SPARSE: one read fewer in flight (registers)
     auto op_a = [&](int j2) __attribute__((always_inline)) {  // j2: sub-tile j2 / NA, k-step (j2 % NA) / 2, K or V
       return rd.rows((j2 & 1) ? vb : kb, (j2 % NA) >> 1, j2 / NA);
     };
