@@ -336,17 +336,22 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) lb[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[kk][e], ones, lb[e & 1], false);
   };
-  auto pv_step = [&](const unsigned char* vb, int i) __attribute__((always_inline)) {
+  auto pv_read = [&](const unsigned char* vb, int i) __attribute__((always_inline)) {
     const int kk = i / T::DSUB, ds = i % T::DSUB;
     const u32x2_t a0 = lds_tr_read(vb, v_rd[ds] + 16 * kk * T::ROW);
     const u32x2_t a1 = lds_tr_read(vb, v_rd[ds] + (16 * kk + 8) * T::ROW);
-    const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+  };
+  u32x4_t vpre[2];  // the first two Vᵀ operands of a clean matrix phase, read before its barrier
+  auto pv_mma = [&](int i, const u32x4_t& a) __attribute__((always_inline)) {
+    const int kk = i / T::DSUB, ds = i % T::DSUB;
     const bf16x8_t pb = __builtin_shufflevector(__builtin_shufflevector(pw[kk][0], pw[kk][1], 0, 1, 2, 3),
                                                 __builtin_shufflevector(pw[kk][2], pw[kk][3], 0, 1, 2, 3), 0, 1, 2,
                                                 3, 4, 5, 6, 7);
     acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[ds], 0, 0, 0);
     if (ds == T::DSUB - 1) lb_step(kk);
   };
+  auto pv_step = [&](const unsigned char* vb, int i) __attribute__((always_inline)) { pv_mma(i, pv_read(vb, i)); };
   constexpr int NQK = T::KS_QK * T::NSUB;  // MFMAs of one Sᵀ tile
   constexpr int NPV = T::KS_PV * T::DSUB;  // MFMAs of one Oᵀ update
   auto matrix_clean = [&](const unsigned char* vb, const unsigned char* kb) __attribute__((always_inline)) {
@@ -360,14 +365,18 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
     static_assert(NQK == NPV, "interleave pairs one MFMA of each product");
+    // PV(0), PV(1) from the operands read before the barrier, then QK(i) with
+    // PV(i+2): the K reads the first QK waits for run under two MFMAs
+    pv_mma(0, vpre[0]);
+    pv_mma(1, vpre[1]);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       qk_step(kb, i);
-      pv_step(vb, i);
+      if (i + 2 < NPV) pv_step(vb, i + 2);
     }
-    // issue order: the operand reads run kOperandLead MFMA pairs ahead of
-    // their MFMAs (one K read and two Vᵀ transpose reads per pair)
-    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kOperandLead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kOperandLead - 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -445,6 +454,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_fwd_kernel(FwdParams p) {
     else if (active(j))
       softmax(j, std::false_type{});
     wait_vmcnt<4 * T::LOADS>();  // tile j+1
+    // The first two Vᵀ operands of X(j) are read now, ahead of the barrier: V_j
+    // has been visible since the barrier that closed group 1's Y(j-1), which
+    // both groups have passed, and its buffer is refilled only after X(j).
+    if (CLEAN) {
+      vpre[0] = pv_read(vb(P), 0);
+      vpre[1] = pv_read(vb(P), 1);
+    }
     block_barrier();
     // X(j)
     if (CLEAN)
