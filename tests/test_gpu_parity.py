@@ -95,6 +95,22 @@ def test_long_noncausal_sampled_rows():
     _check(w.name + " (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
 
 
+def test_million_keys_causal_sampled_rows():
+    """One head of 2^20 + 77 keys, causal, d = 128: the last workgroup streams
+    16 385 key tiles, and ℓ, ℓ_b and the accumulator sum over a million keys in
+    fp32.  The oracle evaluates sampled rows (the first, the ragged tail, block
+    edges, random ones)."""
+    n = (1 << 20) + 77
+    w = W[2].with_(B=1, H=1, N=n, d=128, causal=True, boost_frac=0.0, wid=200)
+    _say("[case] million keys", n)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, True)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, n - 78, n - 77, n - 2, n - 1], rng.choice(n, 40, replace=False)]))
+    ro, rl = attention_ref(q, k, v, w.scale, True, rows=rows)
+    _check(f"B1 H1 N={n} causal d128 (sampled)", o[:, :, rows], lse[:, :, rows], ro, rl)
+
+
 @pytest.mark.parametrize("n,causal,d", [(4097, True, 128), (4352, True, 64), (4352, False, 64)])
 def test_many_blocks_ragged(n, causal, d):
     """H = 32 with ragged N: more than two query blocks per compute unit and an odd
@@ -290,6 +306,20 @@ def test_decode_short_and_ragged(lkv):
     _check(f"decode L={lkv}", o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), ro, rl)
     if lkv == 1:
         assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+@pytest.mark.parametrize("splits", [64, 1024])
+def test_decode_million_keys(splits):
+    """B1 H4 with 2^20 + 5 keys, d = 128: 64 splits of 16 k keys and 1024 of 1 k,
+    the ragged last split included."""
+    w = W[4].with_(B=1, H=4, lkv=(1 << 20) + 5, wid=210)
+    _say("[case] decode million keys", splits)
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w)
+    ro, rl = decode_ref(q, k, v, w.scale)
+    o, lse = fa.fa_decode(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    _check(f"decode L={w.lkv} splits={splits}", o.float().cpu().numpy()[:, :, 0], lse.cpu().numpy(), ro, rl)
 
 
 # ----------------------------------------------------------------------------
