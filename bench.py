@@ -365,7 +365,7 @@ def main():
     if args.make_traffic:
         return make_traffic(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
               "multi-GPU path; the single-GPU figure is the measurement.", file=sys.stderr)
         return 2
 
