@@ -15,8 +15,9 @@ Pages cited (by title and section; no line numbers):
 * [15-779 L5] "第 5 讲 · 案例：Transformer、注意力与 FlashAttention" — CMU 15-779
   lecture 5 notes (semidirectx.com/notes/courses/cmu15-779/lecture05/).
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed
-forms, a 50-digit brute force, library special cases and invariants; none is
+Every function here is pinned by ``tests/test_oracle.py`` and, for the FP8
+quantisation, ``tests/test_oracle_fp8.py`` against closed forms, a 50-digit
+brute force, library routines and special cases and invariants; none is
 "parity unpinned".
 """
 
@@ -32,6 +33,7 @@ from .ref import (
     masked_probs,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode, bwd_allowance, check_bwd
+from .fp8 import e4m3_round, quantize_blocks, dequantize_blocks, attention_fp8_ref
 
 __all__ = [
     "scores",
