@@ -51,4 +51,8 @@ __all__ = [
     "check_decode",
     "bwd_allowance",
     "check_bwd",
+    "e4m3_round",
+    "quantize_blocks",
+    "dequantize_blocks",
+    "attention_fp8_ref",
 ]
