@@ -111,6 +111,36 @@ def test_million_keys_causal_sampled_rows():
     _check(f"B1 H1 N={n} causal d128 (sampled)", o[:, :, rows], lse[:, :, rows], ro, rl)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_heads_short_sequences(d):
+    """B64 H96 (6144 heads) of 70 keys each, causal: a grid of one ragged query
+    block per head, far more workgroups than the XCD remap's whole rounds; the
+    oracle checks every row of 40 sampled heads."""
+    w = W[1].with_(B=64, H=96, N=70, d=d, causal=True, wid=220 + d)
+    _say("[case] many heads", d)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, True)
+    rng = np.random.default_rng(d)
+    for b, h in zip(rng.choice(w.B, 40), rng.choice(w.H, 40)):
+        ro, rl = attention_ref(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.scale, True)
+        _check(f"many heads d={d} b={b} h={h}", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
+
+
+def test_decode_many_heads():
+    """B256 H64 (16 384 heads), 300 keys, 8 splits: 131 072 split workgroups."""
+    w = W[4].with_(B=256, H=64, lkv=300, wid=230)
+    _say("[case] decode many heads")
+    q = synth.make_decode_q(w)
+    k, v = synth.make_decode_kv(w, device="cuda")
+    o, lse = fa.fa_decode(q.cuda(), k, v, scale=w.scale, num_splits=8)
+    torch.cuda.synchronize()
+    sel = np.random.default_rng(1).choice(w.B, 12, replace=False)
+    idx = torch.from_numpy(sel).cuda()
+    ro, rl = decode_ref(q[sel], k[idx].cpu(), v[idx].cpu(), w.scale)
+    _check("decode B256 H64 L300 (12 sampled sequences)", o[sel].float().cpu().numpy()[:, :, 0], lse[sel].cpu().numpy(),
+           ro, rl)
+
+
 @pytest.mark.parametrize("n,causal,d", [(4097, True, 128), (4352, True, 64), (4352, False, 64)])
 def test_many_blocks_ragged(n, causal, d):
     """H = 32 with ragged N: more than two query blocks per compute unit and an odd
