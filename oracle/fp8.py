@@ -12,13 +12,16 @@ Readings taken here (the page fixes neither the format nor the block shapes):
   code (either sign) is NaN, so the largest finite magnitude is 1.75·2⁸ = 448.
   It is the 8-bit float with the most precision among the OCP formats, and the
   one gfx950's matrix cores read.
-* A block's scale maps its largest magnitude onto 448: s = amax / 448
-  (s = 1 for an all-zero block).  Elements are divided by s and rounded to the
-  nearest E4M3 value, ties to the even code; the largest element lands on 448
-  itself, and anything that would round past 448 saturates there.
-* Blocks are runs of consecutive rows of one (batch, head) slice, all d columns
-  together: Q in blocks of the kernel's query block, K and V in blocks of its
-  key tile.
+* A block's scale is a power of two, the smallest one that brings its largest
+  magnitude to at most 448: s = 2^⌈log2(amax/448)⌉ (s = 1 for an all-zero
+  block), so the largest element lands in (224, 448].  Power-of-two scales are
+  the ones gfx950's matrix cores apply in the product itself (an E8M0 exponent
+  per operand block), and dividing by one is exact.  Elements are divided by s
+  and rounded to the nearest E4M3 value, ties to the even code, saturating at
+  448.
+* Blocks are runs of 64 consecutive rows of one (batch, head) slice, all d
+  columns together, for Q, K and V alike (the kernel's key tile, and a
+  quarter of its query block).
 * The attention that FP8 inputs define is exact attention of the dequantised
   Q̂ = s·q₈, K̂, V̂ (``attention_fp8_ref``).  Rounding the probabilities to FP8
   before the second product is a step of the kernel, not of this definition; its
@@ -74,7 +77,7 @@ def quantize_blocks(x, block_rows):
     """Block-wise quantisation of x [..., N, d] along its row axis.
 
     Rows [i·block_rows, (i+1)·block_rows) of each leading slice share one scale
-    s = amax/448 (1 when the block is all zero); the stored value is
+    s = 2^⌈log2(amax/448)⌉ (1 when the block is all zero); the stored value is
     e4m3_round(x / s).  Returns (x8, scales): x8 with x's shape (the E4M3 values,
     as float64) and scales [..., ⌈N/block_rows⌉]; the dequantised tensor is
     x8 · s of each row's block."""
@@ -86,7 +89,11 @@ def quantize_blocks(x, block_rows):
     for b in range(nb):
         blk = x[..., b * block_rows:(b + 1) * block_rows, :]
         amax = np.abs(blk).max(axis=(-2, -1)) if blk.size else np.zeros(lead)
-        s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        safe = np.where(amax > 0, amax, E4M3_MAX)
+        e = np.ceil(np.log2(safe / E4M3_MAX)).astype(np.int64)
+        e = np.where(safe / np.ldexp(1.0, e) > E4M3_MAX, e + 1, e)       # log2 rounding guard
+        e = np.where(safe / np.ldexp(1.0, e - 1) <= E4M3_MAX, e - 1, e)
+        s = np.where(amax > 0, np.ldexp(1.0, e), 1.0)
         scales[..., b] = s
         x8[..., b * block_rows:(b + 1) * block_rows, :] = e4m3_round(blk / s[..., None, None])
     return x8, scales
@@ -99,7 +106,7 @@ def dequantize_blocks(x8, scales, block_rows):
     return x8 * rep[..., None]
 
 
-def attention_fp8_ref(q, k, v, scale, causal, q_block=256, kv_block=64, rows=None):
+def attention_fp8_ref(q, k, v, scale, causal, q_block=64, kv_block=64, rows=None):
     """Exact attention of block-quantised inputs: Q, K and V are quantised with
     quantize_blocks (Q in blocks of q_block rows, K and V in blocks of kv_block
     keys), dequantised, and fed to attention_ref.  Returns (O, LSE) as float64
