@@ -75,6 +75,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_atomic_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, f, i, vp, sz, vp]
     lib.fa_decode_paged.restype = i
+    lib.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
+    lib.fa_fp8_packed_bytes.restype = sz
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_quantize_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_fwd_tile_pairs.argtypes = [i, i, i]
@@ -413,3 +419,49 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, scale=None, 
     if st != FA_OK:
         raise FaError(st, "fa_decode_paged")
     return o, lse
+
+
+def fa_fp8_packed_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Bytes of the packed FP8 operand buffer for Q, K, V [B, H, N, d] (0 if unsupported)."""
+    return int(load_library().fa_fp8_packed_bytes(B, H, N, d))
+
+
+def fa_quantize_fp8(q, k, v, packed=None):
+    """Block-wise FP8 (E4M3) quantisation of bf16 q, k, v [B, H, N, 128] into the
+    packed operand buffer of fa_fwd_fp8 (a uint8 tensor; allocated when not given).
+    Runs asynchronously on the current stream; returns the buffer."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, H, N, d = q.shape
+    need = fa_fp8_packed_bytes(B, H, N, d)
+    if packed is None:
+        packed = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, packed.data_ptr(),
+                                        packed.numel(), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_quantize_fp8")
+    return packed
+
+
+def fa_fwd_fp8(packed, B, H, N, d=128, scale=None, causal=False, out=None, lse=None):
+    """Attention forward on the FP8 operands fa_quantize_fp8 wrote: returns
+    (o bf16 [B, H, N, d], lse fp32 [B, H, N]).  ``scale`` defaults to fp32(1/sqrt(d))."""
+    torch = _torch()
+    if packed.dtype != torch.uint8 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous uint8 tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=packed.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=packed.device)
+    if packed.numel() < fa_fp8_packed_bytes(B, H, N, d):
+        raise ValueError("packed buffer too small for this shape")
+    st = load_library().fa_fwd_fp8(packed.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                                   int(bool(causal)), _stream_ptr(packed.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return out, lse

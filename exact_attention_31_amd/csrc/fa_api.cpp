@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
+#include "fa_fp8.h"
 #include "fa_internal.h"
 
 namespace {
@@ -344,6 +345,85 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_decode_gqa(q, k, v, o, lse, B, H, H, Lkv, d, nullptr, scale, num_splits, workspace, workspace_bytes,
                        stream);
+}
+
+}  // extern "C"
+
+// ---- FP8 form of the prefill -------------------------------------------------------
+
+namespace {
+
+// Shape checks shared by the two FP8 calls (d = 128 only).
+fa_status fp8_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != fa::kFp8D) return FA_ERR_UNSUPPORTED;
+  const unsigned long long T = (unsigned long long)fa::ceil_div(N, fa::kFp8Block);
+  if (count4(B, H, N, d) == 0 || (unsigned long long)N * d * 2 > 0x7fff0000ull ||
+      (unsigned long long)B * H > (1ull << 24) || (unsigned long long)B * H * T > 0x7fffffffull ||
+      (unsigned long long)B * H * fa::ceil_div(N, fa::kFwdBlockM) > 0x7fffffffull)
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fp8_packed_bytes(int B, int H, int N, int d) {
+  if (fp8_shape(B, H, N, d) != FA_OK) return 0;
+  return fa::fp8_layout(B, H, N, d).total;
+}
+
+fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, void* packed,
+                          size_t packed_bytes, void* stream) {
+  if (!q || !k || !v || !packed) return FA_ERR_NULL;
+  const fa_status sh = fp8_shape(B, H, N, d);
+  if (sh != FA_OK) return sh;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed)) return FA_ERR_ALIGN;
+  const fa::Fp8Layout L = fa::fp8_layout(B, H, N, d);
+  if (packed_bytes < L.total) return FA_ERR_WORKSPACE;
+  const size_t tb = count4(B, H, N, d) * 2;
+  if (overlap(packed, L.total, q, tb) || overlap(packed, L.total, k, tb) || overlap(packed, L.total, v, tb))
+    return FA_ERR_ALIAS;
+  fa::Fp8QuantParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.packed = static_cast<unsigned char*>(packed);
+  p.L = L;
+  p.BH = B * H;
+  p.N = N;
+  p.T = fa::ceil_div(N, fa::kFp8Block);
+  if (fa::launch_fp8_quantize(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+fa_status fa_fwd_fp8(const void* packed, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                     void* stream) {
+  if (!packed || !o || !lse) return FA_ERR_NULL;
+  const fa_status sh = fp8_shape(B, H, N, d);
+  if (sh != FA_OK) return sh;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
+  if (!aligned16(packed) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const fa::Fp8Layout L = fa::fp8_layout(B, H, N, d);
+  const size_t tb = count4(B, H, N, d) * 2, lb = (size_t)B * H * N * 4;
+  if (overlap(o, tb, packed, L.total) || overlap(lse, lb, packed, L.total) || overlap(o, tb, lse, lb))
+    return FA_ERR_ALIAS;
+  fa::Fp8FwdParams p;
+  p.packed = static_cast<const unsigned char*>(packed);
+  p.L = L;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.BH = B * H;
+  p.N = N;
+  p.T = fa::ceil_div(N, fa::kFp8Block);
+  p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
+  const long long total = (long long)p.BH * p.n_qblk;
+  p.xcd_remap = (total % 8 == 0) && ((total / 8) % p.n_qblk == 0);
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  if (fa::launch_fwd_fp8(p, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
 }
 
 }  // extern "C"

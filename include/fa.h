@@ -27,6 +27,8 @@
  *   fa_bwd_atomic  the same gradients in one key-block pass with dQ added up
  *              atomically ([15-779 L5] §7.4): not bit-reproducible.
  *   fa_bwd_block_sparse  backward of fa_fwd_block_sparse.
+ *   fa_quantize_fp8, fa_fwd_fp8  the forward on FP8 (E4M3) operands with
+ *              block-wise scales ([cicada] §4.4.1, FlashAttention-3).
  *
  * Pages cited: [cicada] "已有的几种大模型上下文支持情况" (blog on standard attention
  * and FlashAttention 1–4, cicada.microarchitecture.cn); [15-779 L5] "第 5 讲 ·
@@ -240,6 +242,36 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
                           int B, int Hq, int Hkv, int d, int page_size, int num_pages,
                           const int* block_table, int max_pages, const int* seqlens, float scale,
                           int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- FP8 form of the prefill ([cicada] §4.4.1: block-wise quantisation) ----
+ *
+ * fa_quantize_fp8 turns bf16 Q, K, V [B, H, N, d] (d = 128) into the packed FP8
+ * operand buffer that fa_fwd_fp8 reads.  Every run of 64 rows of one (b, h)
+ * slice of each tensor gets its own scale s = 2^e, e the smallest integer with
+ * (largest |x| of the block) ≤ 448·2^e, clamped to [−127, 127] (e = 0 for an
+ * all-zero block); each element becomes the OCP E4M3FN value nearest to x/s
+ * (ties to even).  The buffer holds, each section 256-byte aligned and in this
+ * order, with T = ⌈N/64⌉: the codes of Q and of K ([B·H][N][d] bytes each); the
+ * codes of V one 64-key tile at a time, transposed, [B·H][T][d][64] bytes, the
+ * 64 keys of a row in the order that the forward's second product reads them
+ * (byte j holds key 32⌊j/16 mod 2⌋ + 8⌊(j mod 16)/4⌋ + 4⌊j/32⌋ + j mod 4 of the
+ * tile; keys past N are zero); then the scales of Q, K and V as int32 E8M0
+ * bytes e + 127, [B·H][T] each.  packed_bytes must be at least
+ * fa_fp8_packed_bytes(B, H, N, d); the buffer may not overlap q, k or v.
+ *
+ * fa_fwd_fp8 computes O [B, H, N, d] (bf16) and L [B, H, N] (fp32) of the
+ * attention these operands define, exact attention of the dequantised
+ * Q̂ = s·q₈, K̂, V̂ with scale and causal as for fa_fwd, except that the
+ * probabilities enter the second product rounded to E4M3 (O is divided by the
+ * sum of the unrounded ones).  Both products run on the FP8 matrix cores with
+ * the block scales applied inside them.  All pointers are device pointers the
+ * caller owns; status codes as for fa_fwd, FA_ERR_UNSUPPORTED for d ≠ 128,
+ * FA_ERR_WORKSPACE for a short buffer. */
+size_t fa_fp8_packed_bytes(int B, int H, int N, int d);
+fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, void* packed,
+                          size_t packed_bytes, void* stream);
+fa_status fa_fwd_fp8(const void* packed, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                     void* stream);
 
 /* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
  * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not

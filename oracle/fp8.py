@@ -13,8 +13,9 @@ Readings taken here (the page fixes neither the format nor the block shapes):
   It is the 8-bit float with the most precision among the OCP formats, and the
   one gfx950's matrix cores read.
 * A block's scale is a power of two, the smallest one that brings its largest
-  magnitude to at most 448: s = 2^⌈log2(amax/448)⌉ (s = 1 for an all-zero
-  block), so the largest element lands in (224, 448].  Power-of-two scales are
+  magnitude to at most 448: s = 2^⌈log2(amax/448)⌉, the exponent clamped to
+  the E8M0 range [−127, 127] (s = 1 for an all-zero block), so the largest
+  element lands in (224, 448].  Power-of-two scales are
   the ones gfx950's matrix cores apply in the product itself (an E8M0 exponent
   per operand block), and dividing by one is exact.  Elements are divided by s
   and rounded to the nearest E4M3 value, ties to the even code, saturating at
@@ -93,6 +94,7 @@ def quantize_blocks(x, block_rows):
         e = np.ceil(np.log2(safe / E4M3_MAX)).astype(np.int64)
         e = np.where(safe / np.ldexp(1.0, e) > E4M3_MAX, e + 1, e)       # log2 rounding guard
         e = np.where(safe / np.ldexp(1.0, e - 1) <= E4M3_MAX, e - 1, e)
+        e = np.clip(e, -127, 127)                                        # the E8M0 range
         s = np.where(amax > 0, np.ldexp(1.0, e), 1.0)
         scales[..., b] = s
         x8[..., b * block_rows:(b + 1) * block_rows, :] = e4m3_round(blk / s[..., None, None])
@@ -115,3 +117,51 @@ def attention_fp8_ref(q, k, v, scale, causal, q_block=64, kv_block=64, rows=None
     kh = dequantize_blocks(*quantize_blocks(k, kv_block), kv_block)
     vh = dequantize_blocks(*quantize_blocks(v, kv_block), kv_block)
     return attention_ref(qh, kh, vh, scale, causal, rows=rows)
+
+
+def fp8_allowance(q, k, v, scale, causal, block=64, rows=None):
+    """The parity bound of the FP8 forward, per output row.
+
+    The kernel rounds each probability P̃_i = exp(s_i − m) (m at most the row's
+    true max, so P̃_i ≤ 2^8 is the only range it needs) to E4M3 before the second
+    product and divides by the fp32 sum ℓ of the unrounded P̃.  E4M3 rounding
+    moves a value by at most 2^−4 of itself (3 mantissa bits) or by 2^−10 (half
+    the subnormal spacing), whichever is larger; a later rescale by α ≤ 1 only
+    shrinks both.  With p_i = P̃_i/ℓ and ℓ ≥ ℓ* = Σ exp(s_i − max s):
+
+        |O − O_ref| ≤ 2^−4·Σ p_i |v̂_i| + 2^−10·Σ |v̂_i| / ℓ*
+
+    per element of O (v̂ the dequantised values of that column).  Returns
+    (O_ref, L_ref, allowance) as float64 [B, H, R, d], [B, H, R], [B, H, R, d]
+    for the query rows ``rows`` (all by default)."""
+    from .ref import scores, safe_softmax
+    qh = dequantize_blocks(*quantize_blocks(q, block), block)
+    kh = dequantize_blocks(*quantize_blocks(k, block), block)
+    vh = dequantize_blocks(*quantize_blocks(v, block), block)
+    B, H, N, _ = qh.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    o = np.empty((B, H, rows.size, vh.shape[-1]))
+    lse = np.empty((B, H, rows.size))
+    allow = np.empty_like(o)
+    for b in range(B):
+        for h in range(H):
+            s = scores(qh[b, h][rows], kh[b, h], scale, causal, rows)
+            p, m, l = safe_softmax(s)
+            o[b, h] = p @ vh[b, h]
+            lse[b, h] = m + np.log(l)
+            seen = (p > 0).astype(np.float64)  # keys the row attends to (masked ones carry no rounding)
+            allow[b, h] = 2.0 ** -4 * (p @ np.abs(vh[b, h])) + 2.0 ** -10 * (seen @ np.abs(vh[b, h])) / l[:, None]
+    return o, lse, allow
+
+
+def check_fp8(o, lse, o_ref, lse_ref, allow, slack=1e-3, lse_tol=1e-3):
+    """|O − O_ref| ≤ allowance + slack + ½ulp_bf16(O_ref) per element (slack: the
+    fp32 sums and the hardware exp2) and |L − L_ref| ≤ lse_tol.  Returns a
+    report dict with 'pass'."""
+    from .compare import bf16_half_ulp
+    o = np.asarray(o, np.float64)
+    err = np.abs(o - o_ref)
+    lim = allow + slack + bf16_half_ulp(o_ref)
+    lerr = np.abs(np.asarray(lse, np.float64) - lse_ref)
+    return {"pass": bool(np.all(err <= lim) and np.all(lerr <= lse_tol)), "max_abs": float(err.max()),
+            "ratio": float((err / lim).max()), "lse_max_abs": float(lerr.max()), "allow_max": float(allow.max())}

@@ -1,0 +1,120 @@
+"""GPU parity of the FP8 prefill: fa_quantize_fp8 bit for bit against the
+oracle's block-wise E4M3 quantisation (codes, transposed V tiles and E8M0
+scales), and fa_fwd_fp8 against exact attention of the dequantised inputs
+within the bound oracle/fp8.py derives for rounding P̃ to E4M3."""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import exact_attention_31_amd as fa
+import synth
+from oracle.fp8 import check_fp8, e4m3_decode_table, fp8_allowance, quantize_blocks
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+POS = e4m3_decode_table()[:0x7F]  # values of codes 0x00 .. 0x7E
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    fa.load_library()
+    yield
+
+
+def _codes(x):
+    """E4M3 codes of exactly representable float64 values (sign bit from the sign, −0 included)."""
+    a = np.abs(x)
+    c = np.searchsorted(POS, a)
+    assert np.all(POS[np.minimum(c, len(POS) - 1)] == a)
+    return (c | (np.signbit(x) << 7)).astype(np.uint8)
+
+
+def _layout(B, H, N, d=128):
+    pad = lambda n: (n + 255) // 256 * 256
+    bh, T = B * H, -(-N // 64)
+    q8 = 0
+    k8 = q8 + pad(bh * N * d)
+    vt8 = k8 + pad(bh * N * d)
+    qs = vt8 + pad(bh * T * d * 64)
+    ks = qs + pad(bh * T * 4)
+    vs = ks + pad(bh * T * 4)
+    return dict(q8=q8, k8=k8, vt8=vt8, qs=qs, ks=ks, vs=vs, total=vs + pad(bh * T * 4), T=T)
+
+
+def _vt_key(j):
+    return 32 * ((j >> 4) & 1) + 8 * ((j & 15) >> 2) + 4 * (j >> 5) + (j & 3)
+
+
+@pytest.mark.parametrize("N", [1, 64, 200])
+def test_quantize_matches_oracle_bit_for_bit(N):
+    B, H, d = 1, 3, 128
+    w = W[2].with_(B=B, H=H, N=N, d=d, boost_frac=0.02, wid=240 + N)
+    _say("[case] fp8 quantize", N)
+    q, k, v = synth.make_prefill(w)
+    k[0, 1, : min(N, 64)] = 0  # an all-zero block
+    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    L = _layout(B, H, N)
+    assert fa.fa_fp8_packed_bytes(B, H, N, d) == L["total"]
+    buf = packed.cpu().numpy()
+    T = L["T"]
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        x8, s = quantize_blocks(x, 64)
+        sc = buf[L[name + "s"]:L[name + "s"] + B * H * T * 4].view(np.int32).reshape(B, H, T)
+        assert np.array_equal(sc, (np.log2(s) + 127).astype(np.int32)), name
+        if name != "v":
+            got = buf[L[name + "8"]:L[name + "8"] + B * H * N * d].reshape(B, H, N, d)
+            assert np.array_equal(got, _codes(x8)), name
+        else:
+            got = buf[L["vt8"]:L["vt8"] + B * H * T * d * 64].reshape(B, H, T, d, 64)
+            pad = np.zeros((B, H, T * 64, d))
+            pad[:, :, :N] = x8
+            keys = np.array([_vt_key(j) for j in range(64)])
+            want = np.stack([pad[:, :, t * 64 + keys, :].transpose(0, 1, 3, 2) for t in range(T)], axis=2)
+            assert np.array_equal(got, _codes(want)), name
+
+
+def _fwd_case(w, rows=None, heads=None):
+    q, k, v = synth.make_prefill(w)
+    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda())
+    o, lse = fa.fa_fwd_fp8(packed, w.B, w.H, w.N, 128, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    hs = list(range(w.H)) if heads is None else heads
+    ro, rl, allow = fp8_allowance(q[:, hs], k[:, hs], v[:, hs], w.scale, w.causal, rows=rows)
+    og = o[:, hs].float().cpu().numpy()
+    lg = lse[:, hs].cpu().numpy()
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    rep = check_fp8(og, lg, ro, rl, allow)
+    _say(f"[parity-fp8] {w.name} N={w.N} causal={w.causal}: O max_abs={rep['max_abs']:.3g} "
+         f"ratio={rep['ratio']:.3f} (allowance up to {rep['allow_max']:.3g}) LSE max_abs={rep['lse_max_abs']:.3g}")
+    assert rep["pass"], rep
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 64, 65, 300, 513])
+def test_fwd_fp8_against_oracle(N, causal):
+    w = W[2].with_(B=1, H=2, N=N, d=128, causal=causal, boost_frac=0.01, wid=250 + N + causal)
+    _say("[case] fp8 forward", N, causal)
+    _fwd_case(w)
+
+
+def test_fwd_fp8_full_size_sampled():
+    """The prefill workload (B1 H32 N4096 d128 causal, 1 % of key rows ×8):
+    three heads, sampled rows."""
+    w = W[2]
+    _say("[case] fp8 forward full size")
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 4095], np.random.default_rng(3).choice(4096, 60)]))
+    _fwd_case(w, rows=rows, heads=[0, 17, 31])

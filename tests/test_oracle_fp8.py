@@ -141,3 +141,38 @@ def test_fp8_attention_moves_away_from_exact_attention_by_the_rounding():
     o, l = attention_fp8_ref(q, k, v, 0.125, True)
     ro, rl = attention_ref(q, k, v, 0.125, True)
     assert 0 < np.abs(o - ro).max() < 0.25 and np.abs(l - rl).max() < 0.5
+
+
+def _sim_kernel(q, k, v, scale, causal, shift, rng):
+    """The FP8 forward's arithmetic on the CPU: P̃ against a reference max below
+    the true one by up to `shift` (in natural-log units), rounded to E4M3 for the
+    second product, O divided by the sum of the unrounded P̃."""
+    from oracle.fp8 import dequantize_blocks, quantize_blocks
+    from oracle.ref import scores
+    qh, kh, vh = (dequantize_blocks(*quantize_blocks(t, 64), 64) for t in (q, k, v))
+    o = np.empty(qh.shape)
+    for b in range(qh.shape[0]):
+        for h in range(qh.shape[1]):
+            s = scores(qh[b, h], kh[b, h], scale, causal)
+            m = s.max(axis=1) - rng.uniform(0, shift, s.shape[0])
+            pt = np.exp(s - m[:, None])
+            o[b, h] = (e4m3_round(pt) @ vh[b, h]) / pt.sum(axis=1)[:, None]
+    return o
+
+
+def test_fp8_allowance_covers_the_kernel_arithmetic():
+    """Random stale maxima up to the rescale threshold (2^8) and E4M3 weights:
+    the simulated kernel output stays within the bound on every element."""
+    from oracle.fp8 import fp8_allowance
+    rng = np.random.default_rng(17)
+    shape = (1, 2, 200, 128)
+    q = rng.normal(0, 1, shape)
+    k = rng.normal(0, 1, shape)
+    v = rng.normal(0, 1, shape)
+    k[:, :, ::37] *= 6.0  # a few dominant keys: weights near 1 next to many subnormal ones
+    for causal in (False, True):
+        ro, rl, allow = fp8_allowance(q, k, v, 0.125, causal)
+        for shift in (0.0, 8 * np.log(2)):
+            o = _sim_kernel(q, k, v, 0.125, causal, shift, rng)
+            err = np.abs(o - ro)
+            assert np.all(err <= allow * (1 + 1e-9)), (causal, shift, float((err / allow).max()))
