@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "sparse", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "sparse", "fp8", "copy"], default="all",
                     help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
                          "decode and 'bwd' the backward, both measured after the step; 'copy' times a "
                          "plain 1 GiB device-to-device copy, the reference for scaling HBM byte counters")
@@ -251,6 +251,48 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
              "ms": round(pavg, 4), "ms_min": round(min(ms), 4), "frac_hbm_peak": round(pgbs / HBM_PEAK_GBS, 4),
              "vs_contiguous": round(avg / pavg, 3)}
     return res, paged
+
+
+MFMA_FP8_PEAK_TFLOPS = 2 * MFMA_BF16_PEAK_TFLOPS  # dense FP8 matrix rate: twice bf16's
+
+
+def time_fp8(torch, fa, synth, dev, args):
+    """The FP8 prefill on the prefill workload and on the long non-causal one:
+    fa_fwd_fp8 on operands fa_quantize_fp8 wrote beforehand, interleaved with the
+    bf16 fa_fwd on the same inputs, W + K calls each between HIP events; the
+    quantising pass is timed on its own."""
+    res = {}
+    for wname in ("llama3_8b_causal_b1h32n4096d128_kboost", "long_noncausal_b1h16n16384d128"):
+        w = synth.BY_NAME[wname]
+        print(f"[bench] fp8: {w.name}", file=sys.stderr, flush=True)
+        q, k, v = (t.to(dev) for t in synth.make_prefill(w))
+        packed = fa.fa_quantize_fp8(q, k, v)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            fa.fa_quantize_fp8(q, k, v, packed=packed)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record()
+            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            e[1].record()
+            e[2].record()
+            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            e[3].record()
+            e[4].record()
+            fa.fa_quantize_fp8(q, k, v, packed=packed)
+            e[5].record()
+        torch.cuda.synchronize()
+        f8, bf, qz = (sum(e[a].elapsed_time(e[a + 1]) for e in ev) / len(ev) for a in (0, 2, 4))
+        flops = synth.prefill_flops(w)
+        tf = flops / (f8 * 1e-3) / 1e12
+        res[w.name] = {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(f8, 4),
+                       "frac_mfma_fp8_peak": round(tf / MFMA_FP8_PEAK_TFLOPS, 4), "bf16_ms": round(bf, 4),
+                       "speedup_vs_bf16": round(bf / f8, 3), "quantize_ms": round(qz, 4)}
+    return res
 
 
 def time_sparse(torch, fa, synth, dev, args, traffic):
@@ -490,6 +532,8 @@ def main():
         out["backward"] = time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic)
     if args.only in ("all", "sparse"):
         out["block_sparse"] = time_sparse(torch, fa, synth, dev, args, traffic)
+    if args.only in ("all", "fp8"):
+        out["fp8"] = time_fp8(torch, fa, synth, dev, args)
     if not args.no_cpu_baseline and args.only == "all":
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wf, wd, q, k, v, qd, kd, vd, args.cpu_seconds)
