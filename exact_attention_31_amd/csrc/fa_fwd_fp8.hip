@@ -154,7 +154,7 @@ __device__ inline void fp8_decode_work(const Fp8FwdParams& p, int& bh, int& qb) 
 
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kFwdThreads), amdgpu_waves_per_eu(2)))
-void fa_fwd_fp8_kernel(Fp8FwdParams p) {
+void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int* __restrict__ vs_all) {
   using T = Fp8Tile;
   constexpr int SROW = 2 * kFp8D + 16;  // staging row stride of the bf16 output (bytes)
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES],
@@ -180,8 +180,11 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p) {
   const unsigned char* const q8 = p.packed + p.L.q8 + (size_t)bh * N * kFp8D;
   const unsigned char* const k8 = p.packed + p.L.k8 + (size_t)bh * N * kFp8D;
   const unsigned char* const vt8 = p.packed + p.L.vt8 + (size_t)bh * p.T * T::TILE_BYTES;
-  const int* const __restrict__ ksc = reinterpret_cast<const int*>(p.packed + p.L.ks) + (size_t)bh * p.T;
-  const int* const __restrict__ vsc = reinterpret_cast<const int*>(p.packed + p.L.vs) + (size_t)bh * p.T;
+  // The K and V block scales come in as their own read-only kernel arguments, so
+  // that their uniform reads become scalar loads: vector loads here would count
+  // against the tile loads' vmcnt bookkeeping and make each wait cover a tile more.
+  const int* const ksc = ks_all + (size_t)bh * p.T;
+  const int* const vsc = vs_all + (size_t)bh * p.T;
   const int qse = __builtin_amdgcn_readfirstlane(
       reinterpret_cast<const int*>(p.packed + p.L.qs)[(size_t)bh * p.T + min(wq0, N - 1) / kFp8Block]);
 
@@ -424,7 +427,8 @@ template <bool CAUSAL>
 hipError_t launch_fwd_fp8_t(const Fp8FwdParams& p, hipStream_t stream) {
   static const hipError_t attr = allow_full_lds(&fa_fwd_fp8_kernel<CAUSAL>);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p,
+                     reinterpret_cast<const int*>(p.packed + p.L.ks), reinterpret_cast<const int*>(p.packed + p.L.vs));
   return hipGetLastError();
 }
 
