@@ -249,3 +249,42 @@ def test_python_binding_rejects_bad_tensors():
         fa.fa_fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.fa_fwd(q.float(), q, q)
+
+
+def _q8(q=P[0], k=P[1], v=P[2], B=1, H=2, N=300, d=128, pk=P[3], pkb=1 << 30):
+    lib = _lib()
+    lib.fa_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                                   ctypes.c_void_p]
+    return lib.fa_quantize_fp8(q, k, v, B, H, N, d, pk, pkb, None)
+
+
+def _f8(pk=P[3], o=P[4], lse=P[5], B=1, H=2, N=300, d=128, scale=0.1, causal=1):
+    lib = _lib()
+    lib.fa_fwd_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                              ctypes.c_void_p]
+    return lib.fa_fwd_fp8(pk, o, lse, B, H, N, d, scale, causal, None)
+
+
+def test_fp8_packed_bytes_follow_the_documented_layout():
+    lib = _lib()
+    lib.fa_fp8_packed_bytes.argtypes = [ctypes.c_int] * 4
+    lib.fa_fp8_packed_bytes.restype = ctypes.c_size_t
+    pad = lambda n: (n + 255) // 256 * 256
+    B, H, N, d = 2, 3, 300, 128
+    T = -(-N // 64)
+    want = 2 * pad(B * H * N * d) + pad(B * H * T * d * 64) + 3 * pad(B * H * T * 4)
+    assert lib.fa_fp8_packed_bytes(B, H, N, d) == want
+    assert lib.fa_fp8_packed_bytes(B, H, N, 64) == 0 and lib.fa_fp8_packed_bytes(B, H, 0, d) == 0
+
+
+def test_fp8_argument_checks():
+    """Every call here fails validation before any HIP call."""
+    assert _q8(q=None) == 1 and _q8(pk=None) == 1
+    assert _q8(N=0) == 2 and _q8(d=64) == 3
+    assert _q8(pkb=1000) == 6
+    assert _q8(v=MISALIGNED) == 4
+    assert _q8(pk=P[0]) == 8  # the buffer over q
+    assert _f8(pk=None) == 1 and _f8(lse=None) == 1
+    assert _f8(B=0) == 2 and _f8(d=64) == 3 and _f8(scale=0.0) == 5 and _f8(scale=float("nan")) == 5
+    assert _f8(o=MISALIGNED) == 4
+    assert _f8(o=P[3]) == 8  # O over the packed operands
