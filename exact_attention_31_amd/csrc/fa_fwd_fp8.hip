@@ -314,18 +314,10 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
     }
-    if (do_pv && do_qk) {
 #pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        qk_step(kb, i, kse);
-        pv_step(vb, i, vse);
-      }
-    } else if (do_qk) {
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) qk_step(kb, i, kse);
-    } else if (do_pv) {
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) pv_step(vb, i, vse);
+    for (int i = 0; i < NQK; ++i) {
+      if (do_qk) qk_step(kb, i, kse);
+      if (do_pv) pv_step(vb, i, vse);
     }
     __builtin_amdgcn_s_setprio(0);
   };
