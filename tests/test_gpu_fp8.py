@@ -118,3 +118,11 @@ def test_fwd_fp8_full_size_sampled():
     _say("[case] fp8 forward full size")
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 4095], np.random.default_rng(3).choice(4096, 60)]))
     _fwd_case(w, rows=rows, heads=[0, 17, 31])
+
+
+def test_fwd_fp8_long_noncausal_sampled():
+    """B1 H16 N16384 d128 non-causal: two heads, sampled rows (block edges, the last row, random)."""
+    w = W[3]
+    _say("[case] fp8 forward long")
+    rows = np.unique(np.concatenate([[0, 63, 64, 16383], np.random.default_rng(5).choice(16384, 50)]))
+    _fwd_case(w, rows=rows, heads=[3, 12])

@@ -58,12 +58,16 @@ def _inputs(seed):
 
 
 def _step(t, scale, dscale, tbl, lens):
-    """One pass over the entry points: forward, both backward forms, decode, paged decode."""
+    """One pass over the entry points: forward, backward, decode, paged decode, and the FP8
+    quantising pass and forward."""
     o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], scale=scale, causal=True)
     g2 = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale=scale, causal=True)
     od, ld = fa.fa_decode(t["qd"], t["kd"], t["vd"], scale=dscale, num_splits=16)
     op, lp = fa.fa_decode_paged(t["qp"], t["kp"], t["vp"], tbl, seqlens=lens, scale=dscale, num_splits=5)
-    return [o, lse, *g2, od, ld, op, lp]
+    packed = fa.fa_quantize_fp8(t["q"], t["k"], t["v"])
+    B, H, N, d = t["q"].shape
+    o8, l8 = fa.fa_fwd_fp8(packed, B, H, N, d, scale=scale, causal=True)
+    return [o, lse, *g2, od, ld, op, lp, o8, l8]
 
 
 def test_graph_replays_match_eager_on_new_inputs():
@@ -97,6 +101,6 @@ def test_graph_replays_match_eager_on_new_inputs():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        names = ("o", "lse", "dq", "dk", "dv", "o_decode", "lse_decode", "o_paged", "lse_paged")
+        names = ("o", "lse", "dq", "dk", "dv", "o_decode", "lse_decode", "o_paged", "lse_paged", "o_fp8", "lse_fp8")
         for name, a, b in zip(names, outs, want):
             assert _same(a, b), (rep, name)
