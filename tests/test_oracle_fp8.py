@@ -176,3 +176,210 @@ def test_fp8_allowance_covers_the_kernel_arithmetic():
             o = _sim_kernel(q, k, v, 0.125, causal, shift, rng)
             err = np.abs(o - ro)
             assert np.all(err <= allow * (1 + 1e-9)), (causal, shift, float((err / allow).max()))
+
+
+# ---- the kernel-step model and the tight FP8 contract ---------------------------------
+
+from oracle.compare import bf16_rne
+from oracle.fp8 import check_fp8, fp8_contract, fp8_step_model
+
+import synth
+
+LN2 = float(np.log(2.0))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 300])
+def test_step_model_without_rounding_is_the_definition(N, causal):
+    """With P̃ left unrounded the model's reference-max schedule changes nothing
+    in exact arithmetic ([cicada] §5: ℓ and the accumulator share the stale max):
+    O and L equal exact attention of the dequantised inputs."""
+    w = synth.WORKLOADS[2].with_(B=1, H=2, N=N, causal=causal, boost_frac=0.03, wid=900 + N + causal)
+    q, k, v = synth.make_prefill(w)
+    m = fp8_step_model(q, k, v, w.scale, causal, round_p=False)
+    o, l = attention_fp8_ref(q, k, v, w.scale, causal)
+    assert np.allclose(m["o"], o, rtol=1e-12, atol=1e-13) and np.allclose(m["lse"], l, rtol=1e-13, atol=1e-12)
+    if N >= 300:
+        assert m["moves"].max() >= 2  # the boosted keys did move the reference max
+
+
+def _integer_logit_inputs(N, grow_at=None, grow_row=0, grow=9.0, base=3.0):
+    """q̂, k̂ for scale = ln 2 (so the base-2 logits are t = q̂·k̂): t_ij = −(j mod 3);
+    from key ``grow_at`` on every row's logits are ``base`` higher, and those of
+    row ``grow_row`` ``grow`` higher."""
+    d = 128
+    q = np.zeros((1, 1, N, d))
+    k = np.zeros((1, 1, N, d))
+    q[0, 0, :, 0] = 1.0
+    k[0, 0, :, 0] = -(np.arange(N) % 3)
+    q[0, 0, :, 2] = 1.0
+    q[0, 0, grow_row, 1] = 1.0
+    if grow_at is not None:
+        k[0, 0, grow_at:, 2] = base
+        k[0, 0, grow_at:, 1] = grow - base
+    v = np.random.default_rng(N).normal(0, 1, (1, 1, N, d))
+    return q, k, v
+
+
+def test_step_model_is_exact_on_representable_weights():
+    """Logits that are integers in base 2 make every P̃ an exact power of two
+    between 2^-2 and 2^8 (the stale max), all of them E4M3 values: rounding
+    changes nothing, and the model equals the definition, although the keys at
+    +9 (row 250) move the reference max of the row's whole group while the
+    next group, whose rows grow by 3 only, keeps its stale max."""
+    q, k, v = _integer_logit_inputs(300, grow_at=192, grow_row=250)
+    for causal in (False, True):
+        m = fp8_step_model(q, k, v, LN2, causal)
+        o, l = attention_fp8_ref(q, k, v, LN2, causal)
+        assert np.allclose(m["o"], o, rtol=1e-13, atol=1e-14) and np.allclose(m["lse"], l, rtol=1e-14, atol=1e-13)
+        assert np.all(m["amb"] == 0)  # exact weights sit far from every rounding boundary
+        assert np.all(m["moves"][0, 0, 224:256] == 2)          # the group of row 250 moved at the key tile 192
+        assert np.all(m["moves"][0, 0, 256:300] == 1)          # growth 3 only: the stale max is kept
+        assert np.all(m["moves"][0, 0, :192] == 1)
+
+
+def test_step_model_schedule():
+    """The reference max of a 32-row group moves for every row of the group when
+    one row outgrows it by more than 2^8 (growths 9 and 8.5, E4M3-exact after
+    quantisation), not at 7.5, and a growth within the fp32 error bound of the
+    threshold (8 exactly, nudged either way by the scale) is flagged."""
+    cases = [(9.0, 1.0, 2, False), (8.5, 1.0, 2, False), (7.5, 1.0, 1, False),
+             (8.0, 1.0 + 1e-9, 2, True), (8.0, 1.0 - 1e-9, 1, True), (8.0, 1.0, 1, True)]
+    for grow, f, moves, amb in cases:
+        q, k, v = _integer_logit_inputs(300, grow_at=128, grow_row=3, grow=grow)
+        m = fp8_step_model(q, k, v, LN2 * f, False)
+        assert np.all(m["moves"][0, 0, :32] == moves), (grow, f)  # the whole group of row 3
+        assert np.all(m["moves"][0, 0, 32:] == 1), (grow, f)      # other groups: only the first tile
+        assert np.all(m["sched_amb"][0, 0, :32] == amb) and not m["sched_amb"][0, 0, 32:].any(), (grow, f)
+
+
+def test_step_model_within_the_schedule_free_bound():
+    """The model (a particular schedule) stays within fp8_allowance, the bound
+    derived for any stale max up to 2^8 and any E4M3 rounding of P̃."""
+    w = synth.WORKLOADS[2].with_(B=1, H=2, N=400, causal=True, boost_frac=0.02, wid=931)
+    q, k, v = synth.make_prefill(w)
+    for causal in (False, True):
+        con = fp8_contract(q, k, v, w.scale, causal)
+        assert np.all(np.abs(con["o"] - con["o_ref"]) <= con["allow_def"] * (1 + 1e-9))
+
+
+def _sim_fp32_kernel(q, k, v, scale, causal, rows):
+    """A float32 re-enactment of the FP8 forward's arithmetic, written apart from
+    the model: fp32 logits of the dequantised operands, exp2 and sums in fp32,
+    P̃ rounded to E4M3 by torch's float8_e4m3fn conversion, the reference max of
+    each 32-row group moved when one of its rows outgrows it by more than 2^8,
+    O = acc·(1/ℓ) rounded to bf16, L = m·scale + ln ℓ.  Returns (O, L) on the
+    rows of every 32-row group that holds one of ``rows``."""
+    from oracle.fp8 import dequantize_blocks, quantize_blocks
+    qh, kh, vh = (dequantize_blocks(*quantize_blocks(t, 64), 64).astype(np.float32) for t in (q, k, v))
+    B, H, N, d = qh.shape
+    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    groups = np.unique(np.asarray(rows) // 32)
+    outs_o, outs_l, outs_r = [], [], []
+    for g in groups:
+        r = np.arange(32 * g, min(N, 32 * g + 32))
+        o = np.zeros((B, H, r.size, d), np.float32)
+        lse = np.zeros((B, H, r.size), np.float32)
+        for b in range(B):
+            for h in range(H):
+                s = qh[b, h][r] @ kh[b, h].T                         # fp32 logits
+                if causal:
+                    s = np.where(np.arange(N)[None, :] > r[:, None], np.float32(-np.inf), s)
+                m = np.full(r.size, -np.inf, np.float32)
+                ell = np.zeros(r.size, np.float32)
+                acc = np.zeros((r.size, d), np.float32)
+                for j in range(0, N, 64):
+                    st = s[:, j:j + 64]
+                    if not np.isfinite(st).any():
+                        continue
+                    mt = st.max(axis=1)
+                    with np.errstate(invalid="ignore"):
+                        grow = (mt - m) * c
+                    if np.any(grow > np.float32(8.0)):
+                        mn = np.fmax(m, mt)
+                        with np.errstate(invalid="ignore"):
+                            al = np.exp2((m - mn) * c).astype(np.float32)
+                        al = np.where(np.isneginf(m), np.float32(0), al)
+                        ell, acc, m = ell * al, acc * al[:, None], mn
+                    with np.errstate(invalid="ignore"):
+                        x = np.exp2(st * c - (m * c)[:, None]).astype(np.float32)
+                    x = np.where(np.isfinite(st), x, np.float32(0))
+                    x8 = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+                    ell = (ell + x.sum(axis=1, dtype=np.float32)).astype(np.float32)
+                    acc = (acc + x8 @ vh[b, h][j:j + 64]).astype(np.float32)
+                o[b, h] = acc * (np.float32(1) / ell)[:, None]
+                lse[b, h] = m * np.float32(scale) + np.log(ell)
+        outs_o.append(o)
+        outs_l.append(lse)
+        outs_r.append(r)
+    o = torch.from_numpy(np.concatenate(outs_o, axis=2)).to(torch.bfloat16).double().numpy()
+    return o, np.concatenate(outs_l, axis=2).astype(np.float64)
+
+
+# (workload, heads, rows): every FP8 shape the GPU tests use, in small and at full size
+FP8_SHAPES = [(synth.WORKLOADS[2].with_(B=1, H=2, N=n, causal=c, boost_frac=0.01, wid=250 + n + c), [0, 1], None)
+              for n in (1, 7, 64, 65, 300, 513) for c in (False, True)]
+FP8_SHAPES += [(synth.WORKLOADS[2], [17], np.array([0, 40, 2100, 4064, 4095])),      # c3: early and late rows
+               (synth.WORKLOADS[3], [3], np.array([0, 64, 9000, 16383]))]             # long non-causal
+
+
+def _shape_id(s):
+    w, _, rows = s
+    return f"{w.name}-N{w.N}-{'c' if w.causal else 'nc'}" + ("-sampled" if rows is not None else "")
+
+
+def _inputs(w, heads):
+    q, k, v = synth.make_prefill(w)
+    return q[:, heads], k[:, heads], v[:, heads]
+
+
+@pytest.mark.parametrize("shape", [s for s in FP8_SHAPES if s[0].N in (65, 513, 4096, 16384)], ids=_shape_id)
+def test_fp32_kernel_simulation_passes(shape):
+    """An fp32 re-enactment of the kernel's arithmetic meets the tight rule: the
+    step allowance covers fp32 logits, exp2, sums and the output rounding."""
+    w, heads, rows = shape
+    q, k, v = _inputs(w, heads)
+    con = fp8_contract(q, k, v, w.scale, w.causal, rows=rows)
+    o, l = _sim_fp32_kernel(q, k, v, w.scale, w.causal, con["rows"])
+    rep = check_fp8(o, l, con)
+    assert rep["pass"], rep
+    assert rep["sched_amb_rows"] == 0
+
+
+def _slips(q, k, v, w, con):
+    """Outputs of planted slips of the kernel step (each a model run on altered
+    inputs or without the rounding), on the contract's rows."""
+    rows = con["rows"]
+    model = lambda q_, k_, v_, **kw: fp8_step_model(q_, k_, v_, w.scale, w.causal, rows=rows, **kw)
+    N = q.shape[2]
+    out = {"zero O": (np.zeros_like(con["o"]), con["lse_ref"])}
+    T = -(-N // 64)
+    vpad = torch.zeros((*v.shape[:2], T * 64, v.shape[3]), dtype=v.dtype)
+    vpad[:, :, :N] = v  # keys of every V tile in reverse order (the tile padded with zero keys)
+    vp = vpad.reshape(*v.shape[:2], T, 64, v.shape[3]).flip(3).reshape(vpad.shape)[:, :, :N].contiguous()
+    m = model(q, k, vp)
+    out["V keys permuted in a tile"] = (bf16_rne(m["o"]), m["lse"])
+    for name in ("q", "k", "v"):  # one block's scale one exponent too large
+        x = {"q": q.clone(), "k": k.clone(), "v": v.clone()}
+        blk = int(rows[-1]) // 64 if name == "q" else 0
+        x[name][:, :, blk * 64:(blk + 1) * 64] *= 2
+        m = model(x["q"], x["k"], x["v"])
+        out[f"{name} block scale ×2"] = (bf16_rne(m["o"]), m["lse"])
+    if N > 1:  # one key: P̃ = 1 is exact, so rounding it cannot be missed or caught
+        m = model(q, k, v, round_p=False)
+        out["P̃ not rounded"] = (bf16_rne(m["o"]), m["lse"])
+    return out
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=_shape_id)
+def test_fp8_rule_rejects_planted_slips(shape):
+    """Each planted slip of the FP8 step fails the rule at every shape the GPU
+    tests use, including N = 16384 non-causal and the Llama-3-shaped late rows;
+    the faithful model (rounded to bf16) passes."""
+    w, heads, rows = shape
+    q, k, v = _inputs(w, heads)
+    con = fp8_contract(q, k, v, w.scale, w.causal, rows=rows)
+    assert check_fp8(bf16_rne(con["o"]), con["lse_ref"], con)["pass"]
+    for name, (o, l) in _slips(q, k, v, w, con).items():
+        rep = check_fp8(o, l, con)
+        assert not rep["pass"], (name, rep)
