@@ -79,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fp8_packed_bytes.restype = sz
     lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_quantize_fp8.restype = i
-    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
@@ -146,6 +146,34 @@ def _check(t, name, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output tensor: exactly ``shape`` and ``dtype``, contiguous, on ``device``."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_buffer(t, name, device):
+    """A caller-supplied scratch or operand buffer: a contiguous tensor on ``device``;
+    returns its size in bytes (the library checks it against what the call needs)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.numel() * t.element_size()
+
+
 def _stream_ptr(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
@@ -169,8 +197,10 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, H, N), torch.float32, q.device)
     st = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                B, H, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device))
     if st != FA_OK:
@@ -207,6 +237,8 @@ def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None,
         _check(t, n, 4)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v shapes differ")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
     T = -(-N // SPARSE_BLOCK)
     m = _check_mask(block_mask, B * H, T, q.device)
@@ -214,8 +246,10 @@ def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, H, N), torch.float32, q.device)
     st = load_library().fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                             B, H, N, d, float(scale), int(bool(causal)), m.data_ptr(), m.shape[0],
                                             _stream_ptr(q.device))
@@ -245,14 +279,17 @@ def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
         num_splits = default_splits(B * H, L)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     need = fa_decode_workspace_bytes(B, H, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = _check_buffer(workspace, "workspace", q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     st = load_library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   B, H, L, d, float(scale), int(num_splits), workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+                                  wbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_decode")
     return o, lse
@@ -300,14 +337,17 @@ def fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None, workspace=
     if num_splits is None:
         g = Hq // Hkv
         num_splits = default_splits(B * Hkv * (g // _group_width(g)), L)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     need = fa_decode_workspace_bytes(B, Hq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = _check_buffer(workspace, "workspace", q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     st = load_library().fa_decode_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                       B, Hq, Hkv, L, d, sl, float(scale), int(num_splits), workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+                                      wbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_decode_gqa")
     return o, lse
@@ -330,13 +370,13 @@ def _bwd_call(fn, q, k, v, o, lse, do, scale, causal, workspace, block_mask=None
     need = fa_bwd_atomic_workspace_bytes(B, H, N, d) if fn == "fa_bwd_atomic" else fa_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = _check_buffer(workspace, "workspace", q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal))]
     if block_mask is not None:
         args += [block_mask.data_ptr(), block_mask.shape[0]]
-    st = getattr(load_library(), fn)(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                     _stream_ptr(q.device))
+    st = getattr(load_library(), fn)(*args, workspace.data_ptr(), wbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, fn)
     return dq, dk, dv
@@ -407,15 +447,18 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, scale=None, 
     if num_splits is None:
         g = Hq // Hkv
         num_splits = default_splits(B * Hkv * (g // _group_width(g)), L)
+    if not (q.device == k_pages.device == v_pages.device):
+        raise ValueError("q, k_pages, v_pages must be on one device")
     need = fa_decode_workspace_bytes(B, Hq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = _check_buffer(workspace, "workspace", q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     st = load_library().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), o.data_ptr(),
                                         lse.data_ptr(), B, Hq, Hkv, d, page_size, num_pages, t.data_ptr(), max_pages,
                                         sl, float(scale), int(num_splits), workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+                                        wbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_decode_paged")
     return o, lse
@@ -435,12 +478,15 @@ def fa_quantize_fp8(q, k, v, packed=None):
         _check(t, n, 4)
     if not (q.shape == k.shape == v.shape):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
     need = fa_fp8_packed_bytes(B, H, N, d)
     if packed is None:
         packed = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    pbytes = _check_buffer(packed, "packed", q.device)
     st = load_library().fa_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, packed.data_ptr(),
-                                        packed.numel(), _stream_ptr(q.device))
+                                        pbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_quantize_fp8")
     return packed
@@ -450,18 +496,21 @@ def fa_fwd_fp8(packed, B, H, N, d=128, scale=None, causal=False, out=None, lse=N
     """Attention forward on the FP8 operands fa_quantize_fp8 wrote: returns
     (o bf16 [B, H, N, d], lse fp32 [B, H, N]).  ``scale`` defaults to fp32(1/sqrt(d))."""
     torch = _torch()
-    if packed.dtype != torch.uint8 or not packed.is_contiguous():
-        raise ValueError("packed must be a contiguous uint8 tensor")
+    if not isinstance(packed, torch.Tensor) or packed.dtype != torch.uint8:
+        raise TypeError("packed must be a uint8 tensor")
+    if packed.device.type != "cuda":
+        raise ValueError(f"packed must be on a ROCm device, got {packed.device}")
+    pbytes = _check_buffer(packed, "packed", packed.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=packed.device)
+    _check_out(out, "out", (B, H, N, d), torch.bfloat16, packed.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=packed.device)
-    if packed.numel() < fa_fp8_packed_bytes(B, H, N, d):
-        raise ValueError("packed buffer too small for this shape")
-    st = load_library().fa_fwd_fp8(packed.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
-                                   int(bool(causal)), _stream_ptr(packed.device))
+    _check_out(lse, "lse", (B, H, N), torch.float32, packed.device)
+    st = load_library().fa_fwd_fp8(packed.data_ptr(), pbytes, out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                   float(scale), int(bool(causal)), _stream_ptr(packed.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
     return out, lse

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -398,14 +398,15 @@ fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, in
   return FA_OK;
 }
 
-fa_status fa_fwd_fp8(const void* packed, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
-                     void* stream) {
+fa_status fa_fwd_fp8(const void* packed, size_t packed_bytes, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, void* stream) {
   if (!packed || !o || !lse) return FA_ERR_NULL;
   const fa_status sh = fp8_shape(B, H, N, d);
   if (sh != FA_OK) return sh;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
-  if (!aligned16(packed) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   const fa::Fp8Layout L = fa::fp8_layout(B, H, N, d);
+  if (packed_bytes < L.total) return FA_ERR_WORKSPACE;
+  if (!aligned16(packed) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   const size_t tb = count4(B, H, N, d) * 2, lb = (size_t)B * H * N * 4;
   if (overlap(o, tb, packed, L.total) || overlap(lse, lb, packed, L.total) || overlap(o, tb, lse, lb))
     return FA_ERR_ALIAS;

@@ -265,13 +265,15 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
  * probabilities enter the second product rounded to E4M3 (O is divided by the
  * sum of the unrounded ones).  Both products run on the FP8 matrix cores with
  * the block scales applied inside them.  All pointers are device pointers the
- * caller owns; status codes as for fa_fwd, FA_ERR_UNSUPPORTED for d ≠ 128,
- * FA_ERR_WORKSPACE for a short buffer. */
+ * caller owns; packed_bytes is the size of the packed buffer, which must be
+ * at least fa_fp8_packed_bytes(B, H, N, d) and hold what fa_quantize_fp8 wrote
+ * for the same B, H, N.  Status codes as for fa_fwd, FA_ERR_UNSUPPORTED for
+ * d ≠ 128, FA_ERR_WORKSPACE for a short buffer. */
 size_t fa_fp8_packed_bytes(int B, int H, int N, int d);
 fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, void* packed,
                           size_t packed_bytes, void* stream);
-fa_status fa_fwd_fp8(const void* packed, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
-                     void* stream);
+fa_status fa_fwd_fp8(const void* packed, size_t packed_bytes, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, void* stream);
 
 /* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
  * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not
@@ -288,7 +290,8 @@ fa_status fa_fwd_tile_shape(int d, int* block_m, int* block_n);
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(int status);
 
-/* ABI version of this header (bumped on incompatible changes). */
+/* ABI version of this header (bumped on incompatible changes; 2: fa_fwd_fp8
+ * takes the packed buffer's size). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

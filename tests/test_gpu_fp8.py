@@ -131,5 +131,5 @@ def test_fwd_fp8_long_noncausal_sampled():
     rows (block edges, the last row, random ones)."""
     w = W[3]
     _say("[case] fp8 forward long")
-    rows = np.unique(np.concatenate([[0, 63, 64, 16383], np.random.default_rng(5).choice(16384, 50)]))
+    rows = np.unique(np.concatenate([[0, 63, 64, 16383], np.random.default_rng(5).choice(16384, 10)]))
     _fwd_case(w, rows=rows, heads=[3, 12])

@@ -95,6 +95,27 @@ def test_long_noncausal_sampled_rows():
     _check(w.name + " (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
 
 
+def test_long_noncausal_full():
+    """N = 16384, all 16 heads, every row compared with the oracle (one head, 4096
+    rows at a time, on the host)."""
+    w = W[3]
+    _say("[case] workload", w.name, "(every row of every head)")
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    worst = None
+    for h in range(w.H):
+        for r0 in range(0, w.N, 4096):
+            rows = np.arange(r0, min(w.N, r0 + 4096))
+            ro, rl = attention_ref(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.scale, False, rows=rows)
+            rep = check_prefill(o[:, h:h + 1, rows], lse[:, h:h + 1, rows], ro, rl)
+            assert rep["pass"], (h, r0, rep)
+            if worst is None or rep["excess"] > worst["excess"]:
+                worst = dict(rep, head=h)
+        _say(f"  head {h}: ok")
+    _say(f"[parity] {w.name} (all 16 x 16384 rows): worst head {worst['head']}: O max_abs={worst['max_abs']:.3g} "
+         f"floor={worst['floor']:.3g} excess={worst['excess']:.3g} LSE max_abs={worst['lse_max_abs']:.3g}")
+
+
 def test_million_keys_causal_sampled_rows():
     """One head of 2^20 + 77 keys, causal, d = 128: the last workgroup streams
     16 385 key tiles, and ℓ, ℓ_b and the accumulator sum over a million keys in
@@ -171,6 +192,30 @@ def test_decode_full_size_sampled_heads():
     for b, h in picks:
         ro, rl = decode_ref(q[b:b + 1, h:h + 1].cpu(), k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu(), w.scale)
         _check(f"{w.name} b{b} h{h}", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
+
+
+def test_decode_full_size_every_head():
+    """B16 H32 Lkv 32768 d128, 64 splits: all 512 (b, h) heads against the unsplit
+    oracle (one sequence's K/V copied to the host at a time)."""
+    w = W[4]
+    _say("[case] workload", w.name, "(every head)")
+    q = synth.make_decode_q(w).cuda()
+    k, v = synth.make_decode_kv(w, device="cuda")
+    o, lse = fa.fa_decode(q, k, v, scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[:, :, 0]
+    lse = lse.cpu().numpy()
+    qh = q.cpu()
+    worst = None
+    for b in range(w.B):
+        ro, rl = decode_ref(qh[b:b + 1], k[b:b + 1].cpu(), v[b:b + 1].cpu(), w.scale)
+        rep = check_prefill(o[b:b + 1], lse[b:b + 1], ro, rl)
+        assert rep["pass"], (b, rep)
+        if worst is None or rep["excess"] > worst["excess"]:
+            worst = dict(rep, b=b)
+    _say(f"[parity] {w.name} (all 512 heads): worst sequence {worst['b']}: O max_abs={worst['max_abs']:.3g} "
+         f"floor={worst['floor']:.3g} excess={worst['excess']:.3g} LSE max_abs={worst['lse_max_abs']:.3g}")
+    del k, v
 
 
 # ----------------------------------------------------------------------------
@@ -372,6 +417,66 @@ def test_canaries_and_guard_bands():
     assert torch.isnan(lbuf[:guard]).all() and torch.isnan(lbuf[-guard:]).all()
 
 
+def _guarded(n, dtype, guard=4096):
+    """A NaN-filled device buffer of n elements with ``guard`` NaN elements on either side."""
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=dtype, device="cuda")
+    return buf, buf[guard:guard + n], guard
+
+
+def _intact(buf, guard, n):
+    return bool(torch.isnan(buf[:guard]).all()) and bool(torch.isnan(buf[guard + n:]).all())
+
+
+@pytest.mark.parametrize("splits", [1, 7])
+def test_decode_canaries_and_guard_bands(splits):
+    """fa_decode (called through the C ABI) writes every element of O and L and
+    nothing around them, nor past its workspace (NaN canaries everywhere)."""
+    w = W[4].with_(B=3, H=5, lkv=1000, wid=112 + splits)
+    q = synth.make_decode_q(w).cuda()
+    k, v = synth.make_decode_kv(w, device="cuda")
+    n_o, n_l = q.numel(), w.B * w.H
+    obuf, o, g = _guarded(n_o, torch.bfloat16)
+    lbuf, l, _ = _guarded(n_l, torch.float32)
+    need = fa.fa_decode_workspace_bytes(w.B, w.H, w.d, splits)
+    wbuf, ws, _ = _guarded(need // 4, torch.float32)
+    st = fa.load_library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), w.B, w.H,
+                                     w.lkv, w.d, w.scale, splits, ws.data_ptr(), need, None)
+    torch.cuda.synchronize()
+    assert st == fa.FA_OK
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    assert _intact(obuf, g, n_o) and _intact(lbuf, g, n_l) and _intact(wbuf, g, need // 4)
+    ro, rl = decode_ref(q.cpu(), k.cpu(), v.cpu(), w.scale)
+    _check(f"decode canaries splits={splits}", o.view(w.B, w.H, w.d).float().cpu().numpy(),
+           l.view(w.B, w.H).cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_atomic"])
+def test_bwd_canaries_and_guard_bands(fn):
+    """The backward (through the C ABI) writes every element of dQ, dK, dV and
+    nothing around them or past its workspace."""
+    w = W[1].with_(B=1, H=2, N=333, d=128, causal=True, wid=114)
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    do = synth.make_prefill_grad(w).cuda()
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=True)
+    n = q.numel()
+    bufs = [_guarded(n, torch.bfloat16) for _ in range(3)]
+    need = (fa.fa_bwd_atomic_workspace_bytes(w.B, w.H, w.N, w.d) if fn == "fa_bwd_atomic"
+            else fa.fa_bwd_workspace_bytes(w.B, w.H, w.N))
+    wbuf, ws, g = _guarded(need // 4, torch.float32)
+    st = getattr(fa.load_library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                       lse.data_ptr(), *[b[1].data_ptr() for b in bufs], w.B, w.H, w.N, w.d, w.scale,
+                                       1, ws.data_ptr(), need, None)
+    torch.cuda.synchronize()
+    assert st == fa.FA_OK
+    ref = fa.fa_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for (buf, x, gb), r in zip(bufs, ref):
+        assert torch.isfinite(x).all() and _intact(buf, gb, n)
+        if fn == "fa_bwd":
+            assert torch.equal(x.view(r.shape), r)   # deterministic: the binding's call gives the same bits
+    assert _intact(wbuf, g, need // 4)
+
+
 def test_deterministic():
     w = W[2].with_(H=4, N=1500, wid=120)
     q, k, v = (t.cuda() for t in synth.make_prefill(w))
@@ -398,3 +503,40 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_binding_rejects_bad_outputs_and_buffers():
+    """Caller-supplied out=, lse=, workspace and packed tensors are checked for
+    shape, dtype, device and contiguity before the library is called."""
+    w = W[0]
+    q, k, v = (t.cuda() for t in synth.make_prefill(w))
+    B, H, N, d = q.shape
+    good_o, good_l = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    bad = [
+        (dict(out=torch.empty((B, H, N - 1, d), dtype=torch.bfloat16, device="cuda")), ValueError),
+        (dict(out=torch.empty_like(q).float()), TypeError),
+        (dict(out=torch.empty_like(q, device="cpu")), ValueError),
+        (dict(out=torch.empty((B, H, d, N), dtype=torch.bfloat16, device="cuda").transpose(2, 3)), ValueError),
+        (dict(lse=torch.empty((B, H, N - 1), dtype=torch.float32, device="cuda")), ValueError),
+        (dict(lse=torch.empty((B, H, N), dtype=torch.float64, device="cuda")), TypeError),
+        (dict(lse=torch.empty((B, H, N), dtype=torch.float32)), ValueError),
+    ]
+    for kw, err in bad:
+        args = dict(out=good_o, lse=good_l)
+        args.update(kw)
+        with pytest.raises(err):
+            fa.fa_fwd(q, k, v, scale=w.scale, **args)
+    wd = W[4].with_(B=1, H=2, lkv=100, wid=130)
+    qd = synth.make_decode_q(wd).cuda()
+    kd, vd = synth.make_decode_kv(wd, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fa_decode(qd, kd, vd, num_splits=4, workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    with pytest.raises(fa.FaError):  # too small: the library's own check
+        fa.fa_decode(qd, kd, vd, num_splits=4, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    q8, k8, v8 = (t.cuda() for t in synth.make_prefill(W[2].with_(B=1, H=1, N=64, wid=131)))
+    packed = fa.fa_quantize_fp8(q8, k8, v8)
+    with pytest.raises(fa.FaError):  # the packed buffer is for N = 64, not 128
+        fa.fa_fwd_fp8(packed, 1, 1, 128, 128)
+    with pytest.raises(ValueError):
+        fa.fa_quantize_fp8(q8, k8, v8, packed=torch.empty_like(packed, device="cpu"))
+    torch.cuda.synchronize()
