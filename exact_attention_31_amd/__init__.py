@@ -10,6 +10,7 @@ library is missing or fails to load, the calls raise.
     fa_decode(q, k, v, scale=None, num_splits=None)  -> (o, lse)
     fa_decode_gqa(q, k, v, seqlens=None, scale=None, num_splits=None) -> (o, lse)
     fa_decode_paged(q, k_pages, v_pages, block_table, seqlens=None, ...) -> (o, lse)
+    fa_decode_noalloc(q, k, v, out, lse, scale=None, num_splits=None) -> (out, lse)
     fa_decode_workspace_bytes(B, H, d, num_splits)   -> int
     fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False) -> (o, lse)
     fa_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
@@ -59,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, vp, sz, vp]
     lib.fa_decode_gqa.restype = i
     lib.fa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
@@ -293,6 +296,40 @@ def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
     if st != FA_OK:
         raise FaError(st, "fa_decode")
     return o, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fa_decode_noalloc(q, k, v, out, lse, scale=None, num_splits=None):
+    """fa_decode for callers that cannot allocate: the caller passes the outputs
+    (out bf16 [B, H, 1, d], lse fp32 [B, H]); the split partials go to the
+    library's own per-GPU scratch (DECODE_NOALLOC_SCRATCH_BYTES), so nothing is
+    allocated.  Calls that may overlap on one GPU race on that scratch.
+    Returns (out, lse)."""
+    torch = _torch()
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    _check(v, "v", 4)
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence, q has {one}")
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    _check_out(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_out(lse, "lse", (B, H), torch.float32, q.device)
+    L = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = default_splits(B * H, L)
+    st = load_library().fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                          B, H, L, d, float(scale), int(num_splits), _stream_ptr(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_noalloc")
+    return out, lse
 
 
 def default_splits(groups: int, L: int) -> int:

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int kAbiVersion = 2;
+static_assert(FA_DECODE_NOALLOC_SCRATCH_BYTES == fa::kDecodeScratchBytes, "the header states the scratch size");
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -260,7 +261,7 @@ namespace {
 fa_status decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int Lmax, int d, const int* seqlens, float scale, int num_splits, void* workspace,
                       size_t workspace_bytes, const int* block_table, int max_pages, int page_shift, int num_pages,
-                      void* stream) {
+                      void* stream, bool check_only = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -270,27 +271,32 @@ fa_status decode_impl(const void* q, const void* k, const void* v, void* o, floa
     return FA_ERR_SHAPE;
   if (block_table && (unsigned long long)num_pages * Hkv << page_shift > 0x7fffffffull) return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f) || num_splits < 1 || num_splits > Lmax) return FA_ERR_VALUE;
+  // check_only: every check except those of the workspace, which the caller
+  // supplies afterwards (the allocation-free call's own scratch)
   const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+  const size_t wb = check_only ? 0 : need;
+  if (!check_only && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (!check_only && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
     return FA_ERR_ALIGN;
   const size_t qb = (size_t)B * Hq * d * 2, kb = kv_elems * 2, lb = (size_t)B * Hq * 4;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) || overlap(lse, lb, q, qb) ||
       overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(o, qb, lse, lb) ||
-      overlap(workspace, need, q, qb) || overlap(workspace, need, k, kb) || overlap(workspace, need, v, kb) ||
-      overlap(workspace, need, o, qb) || overlap(workspace, need, lse, lb))
+      overlap(workspace, wb, q, qb) || overlap(workspace, wb, k, kb) || overlap(workspace, wb, v, kb) ||
+      overlap(workspace, wb, o, qb) || overlap(workspace, wb, lse, lb))
     return FA_ERR_ALIAS;
   if (seqlens) {
     const size_t sb = (size_t)B * 4;
-    if (overlap(o, qb, seqlens, sb) || overlap(lse, lb, seqlens, sb) || overlap(workspace, need, seqlens, sb))
+    if (overlap(o, qb, seqlens, sb) || overlap(lse, lb, seqlens, sb) || overlap(workspace, wb, seqlens, sb))
       return FA_ERR_ALIAS;
   }
   if (block_table) {
     const size_t tb = (size_t)B * max_pages * 4;
-    if (overlap(o, qb, block_table, tb) || overlap(lse, lb, block_table, tb) || overlap(workspace, need, block_table, tb))
+    if (overlap(o, qb, block_table, tb) || overlap(lse, lb, block_table, tb) || overlap(workspace, wb, block_table, tb))
       return FA_ERR_ALIAS;
   }
+  if (check_only) return FA_OK;
 
   fa::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -345,6 +351,19 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     int d, float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_decode_gqa(q, k, v, o, lse, B, H, H, Lkv, d, nullptr, scale, num_splits, workspace, workspace_bytes,
                        stream);
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lkv,
+                            int d, float scale, int num_splits, void* stream) {
+  // every check of fa_decode except the workspace's, then the scratch limit, before any HIP call
+  const fa_status pre = decode_impl(q, k, v, o, lse, B, H, H, Lkv, d, nullptr, scale, num_splits, nullptr, 0,
+                                    nullptr, 0, 0, 0, stream, /*check_only=*/true);
+  if (pre != FA_OK) return pre;
+  if (fa_decode_workspace_bytes(B, H, d, num_splits) > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  return decode_impl(q, k, v, o, lse, B, H, H, Lkv, d, nullptr, scale, num_splits, ws, fa::kDecodeScratchBytes,
+                     nullptr, 0, 0, 0, stream);
 }
 
 }  // extern "C"

@@ -35,6 +35,8 @@
 // segment.
 
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <math.h>
 #include <stdint.h>
 
@@ -358,6 +360,33 @@ hipError_t launch_decode_d(const DecodeParams& p, int B, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream) {
   return d == 64 ? launch_decode_d<64>(p, B, stream) : launch_decode_d<128>(p, B, stream);
+}
+
+// Scratch of the allocation-free decode call (fa_decode_noalloc): the split
+// partials live in this file-scope device array, one copy per GPU, held until
+// the process ends.  In host code the name stands for a host-side shadow, not
+// a device address; the device address is looked up once per device with
+// hipGetSymbolAddress and kept.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

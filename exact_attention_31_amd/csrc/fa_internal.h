@@ -121,4 +121,10 @@ hipError_t launch_fwd(const FwdParams& p, int d, int causal, hipStream_t stream)
 hipError_t launch_bwd(const BwdParams& p, int d, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int B, int d, hipStream_t stream);
 
+// The allocation-free decode call's scratch: a file-scope device array of
+// kDecodeScratchBytes (fa_decode.hip); decode_scratch gives its address on the
+// current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

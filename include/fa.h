@@ -196,6 +196,23 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Lkv, int d, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* fa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments and result without the workspace.  The per-split partials go
+ * to a scratch array of FA_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB) that the
+ * library keeps in device memory, one per GPU, for the life of the process;
+ * the call itself allocates and frees nothing.  Needs
+ * fa_decode_workspace_bytes(B, H, d, num_splits) ≤ that size, else
+ * FA_ERR_WORKSPACE (the decode workload B16 H32 d128 with 64 splits needs
+ * 16.9 MB).  Nothing in the scratch has to start at zero (every partial is
+ * written before it is read).  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (different streams, other host
+ * threads) race and must be ordered by the caller.  Other errors as for
+ * fa_decode; FA_ERR_LAUNCH also when the scratch's address cannot be found. */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Lkv, int d, float scale, int num_splits, void* stream);
+
 /* Grouped-query split-KV decode with per-sequence key counts.
  *   q, o    : bf16 [B, Hq, 1, d].
  *   k, v    : bf16 [B, Hkv, Lmax, d], contiguous per (b, K/V head).  Hq must

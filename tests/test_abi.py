@@ -289,3 +289,21 @@ def test_fp8_argument_checks():
     assert _f8(o=MISALIGNED) == 4
     assert _f8(o=P[3]) == 8  # O over the packed operands
     assert _f8(pkb=1000) == 6  # a packed buffer smaller than the layout needs
+
+
+def _dn(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=512, L=128, d=128, scale=0.1, S=64):
+    lib = _lib()
+    return lib.fa_decode_noalloc(q, k, v, o, lse, B, H, L, d, scale, S, None)
+
+
+def test_decode_noalloc_argument_checks():
+    """The allocation-free decode validates like fa_decode and rejects partials
+    beyond its scratch (32 MiB) before any HIP call."""
+    assert fa.DECODE_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert _dn(q=None) == 1 and _dn(lse=None) == 1
+    assert _dn(B=0) == 2 and _dn(d=96) == 3 and _dn(scale=-1.0) == 5 and _dn(S=0) == 5 and _dn(S=129) == 5
+    assert _dn(o=MISALIGNED) == 4
+    assert _dn(o=P[0]) == 8  # the output over q
+    assert fa.fa_decode_workspace_bytes(16, 32, 128, 64) <= fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_bytes(1, 512, 128, 128) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert _dn(S=128) == 6  # partials of 33.8 MB do not fit (K and V: 16.8 MB each)
