@@ -22,6 +22,11 @@ Each call is also timed with HIP events recorded on the stream it runs on
   * backward         fa_bwd on the prefill workload (the step's O and L, a
                      seeded dO), timed on its own after the step: TFLOP/s of
                      the five N×N×d products, 10·N²·d·B·H / 2 (causal)
+  * prefill_workloads  fa_fwd on each prefill workload (B1 H1 N256 d64; B8 H12
+                     N1024 d64 causal; the Llama-3-shaped one; B1 H16 N16384 d128),
+                     timed warm (back to back) and cold (caches flushed between calls)
+  * device           name, architecture, ROCm and HIP versions, and the gfx clock
+                     amd-smi reports while the prefill runs
   * cpu_baseline     the fp64 oracle on a bounded sample of the same workload,
                      on this host's cores (rank 0, N=1 only)
 Prints one JSON line.
@@ -47,7 +52,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "sparse", "fp8", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "gqa", "bwd", "sparse", "fp8", "copy", "workloads"],
+                    default="all",
                     help="time one call kind only (for counter collection); 'gqa' is the grouped-query "
                          "decode and 'bwd' the backward, both measured after the step; 'copy' times a "
                          "plain 1 GiB device-to-device copy, the reference for scaling HBM byte counters")
@@ -251,6 +257,104 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
              "ms": round(pavg, 4), "ms_min": round(min(ms), 4), "frac_hbm_peak": round(pgbs / HBM_PEAK_GBS, 4),
              "vs_contiguous": round(avg / pavg, 3)}
     return res, paged
+
+
+def device_facts(torch):
+    """Device name, architecture, compute units and the ROCm / HIP versions."""
+    props = torch.cuda.get_device_properties(0)
+    facts = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count,
+             "hip_runtime": torch.version.hip}
+    try:
+        facts["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        facts["rocm"] = None
+    return facts
+
+
+def sample_gfx_clock(run, seconds=1.0):
+    """The shader (gfx) clock while ``run()`` keeps the GPU busy: amd-smi's per-XCD
+    current gfx clock, sampled from a second thread about every 0.1 s."""
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-g", "0", "--clock", "--json"], capture_output=True, text=True,
+                                   timeout=5)
+                data = json.loads(r.stdout)
+                clk = data["gpu_data"][0]["clock"] if isinstance(data, dict) else data[0]["clock"]
+                vals = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+                vals = [float(x) for x in vals if isinstance(x, (int, float))]
+                if vals and statistics.median(vals) >= 500:  # below the lowest level: idle, between calls
+                    samples.append(statistics.median(vals))
+            except Exception:
+                pass
+            stop.wait(0.1)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run()
+    stop.set()
+    th.join(timeout=10)
+    if not samples:
+        return None
+    return {"median_mhz": statistics.median(samples), "min_mhz": min(samples), "max_mhz": max(samples),
+            "samples": len(samples), "source": "amd-smi metric --clock (median over the 8 XCDs per sample) "
+                                               "while the Llama-3-shaped prefill ran back to back"}
+
+
+def time_prefill_workloads(torch, fa, synth, dev, args):
+    """Every prefill workload on its own, each call between HIP events: warm (the
+    calls back to back, inputs in the caches where they fit) and cold (a 512 MB
+    buffer written between calls, outside the timed region)."""
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for w in synth.WORKLOADS[:4]:
+        print(f"[bench] prefill workload: {w.name}", file=sys.stderr, flush=True)
+        q, k, v = (t.to(dev) for t in synth.make_prefill(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        call = lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        warm = [e[0].elapsed_time(e[1]) for e in ev]
+        for i, e in enumerate(ev):
+            scrub.fill_(i & 255)
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        cold = [e[0].elapsed_time(e[1]) for e in ev]
+        flops = synth.prefill_flops(w)
+        ent = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "algorithmic_flops": flops,
+               "algorithmic_bytes": synth.prefill_bytes(w)}
+        for label, ms in (("warm", warm), ("cold", cold)):
+            avg = sum(ms) / len(ms)
+            tf = flops / (avg * 1e-3) / 1e12
+            ent[label] = {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "tflops": round(tf, 2),
+                          "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if w.N * w.H * w.B <= 256:
+            ent["note"] = "one workgroup: launch-latency bound, no roofline claim"
+        res[w.name] = ent
+        del q, k, v, o, lse
+    del scrub
+    return res
 
 
 MFMA_FP8_PEAK_TFLOPS = 2 * MFMA_BF16_PEAK_TFLOPS  # dense FP8 matrix rate: twice bf16's
@@ -508,10 +612,12 @@ def main():
             "parallelism": "single GPU",
         },
     }
+    out["device"] = device_facts(torch)
     if f_avg:
         tf = flops / (f_avg * 1e-3) / 1e12
         out["prefill"] = {"ms": round(f_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tf, 2),
-                          "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+                          "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "caches": "cold: each call follows the decode's 8.6 GB stream" if do_d else "warm"}
         out["roofline"] = {"kernel": f"fa_fwd_kernel<{wf.d},{str(wf.causal).lower()}>", "bound": "mfma",
                            "achieved": round(tf, 2),
                            "peak": round(MFMA_BF16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
@@ -526,6 +632,11 @@ def main():
                                   "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_bytes(traffic, "decode"), "algorithmic_bytes": dbytes}
+    if args.only == "all" and f_avg:
+        out["device"]["gfx_clock_during_prefill"] = sample_gfx_clock(
+            lambda: (fa.fa_fwd(q, k, v, scale=wf.scale, causal=wf.causal, out=o, lse=lse), torch.cuda.synchronize()))
+    if args.only in ("all", "workloads"):
+        out["prefill_workloads"] = time_prefill_workloads(torch, fa, synth, dev, args)
     if args.only in ("all", "gqa"):
         out["decode_gqa"], out["decode_paged"] = time_gqa(torch, fa, synth, dev, args, traffic)
     if args.only in ("all", "bwd"):
