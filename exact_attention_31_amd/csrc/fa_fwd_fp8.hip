@@ -12,11 +12,15 @@
 //   Vᵀ tiles by 4-7, three tiles ahead) on FP8 operands.  Both products run on
 //   v_mfma_scale_f32_32x32x64_f8f6f4, whose E8M0 operand scales apply the
 //   block scales inside the product: Sᵀ = (s_k K₈)(s_q Q₈)ᵀ comes out as fp32
-//   logits of the dequantised inputs, and Oᵀ += (s_v V₈ᵀ) P̃₈ᵀ.  P̃ is
-//   rounded to E4M3 for the second product, which needs it bounded below the
-//   format's 448: the reference max is moved whenever a row outgrows it by
-//   2^8 (conditional rescaling, [cicada] §5, with that threshold).  O is
-//   divided by the fp32 row sum ℓ of the unrounded P̃; L = m + ln ℓ.
+//   logits of the dequantised inputs, and Oᵀ += (s_v V₈ᵀ)(2^σ P̃₈)ᵀ.  P̃ is
+//   computed in fp32 against a reference max that moves only when a row
+//   outgrows it by 2^48 (conditional rescaling, [cicada] §5, as in the bf16
+//   kernel), and is then block-quantised itself ([cicada] §4.4.1): each row's
+//   32-key half of the tile — one scale block of the instruction — takes the
+//   power of two 2^σ that brings its sum below 2^8, so its elements land
+//   below E4M3's 448 with full precision, whatever the row's offset from the
+//   reference max.  O is divided by the fp32 row sum ℓ of the unrounded P̃;
+//   L = m + ln ℓ.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,10 +36,12 @@ namespace fa {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr float kFp8RescaleLog2 = 8.0f;   // P̃ ≤ 2^8 < 448
-constexpr float kFp8SumBound = 256.0f;    // a tile row sum at most this bounds each element by 2^8
-constexpr int kE8M0One = 127;             // E8M0 encoding of 1
+constexpr float kFp8RescaleLog2 = 48.0f;          // P̃ ≤ 2^48 against the reference max
+constexpr float kFp8SumBound = 281474976710656.0f;  // 2^48: a lane's sum at most this bounds its elements
+constexpr int kE8M0One = 127;                     // E8M0 encoding of 1
+constexpr int kPScaleLog2 = 8;                    // a scaled P̃ block sums to less than 2^8
 
 // ---- quantisation ---------------------------------------------------------------
 
@@ -231,7 +237,8 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
   f32x16_t s[T::NSUB];
-  i32x8_t pb;  // P̃ of the tile in E4M3, the B operand of the second product
+  i32x8_t pb;      // 2^-σ P̃ of the tile in E4M3, the B operand of the second product
+  int psc = kE8M0One;  // E8M0 scale 127 + σ of this lane's block of pb (see below)
 
   auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
     const int kv0 = j * T::BN;
@@ -245,22 +252,42 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
           if (key > lim) s[sub][r] = -INFINITY;
         }
     }
+    // P̃ against the reference max, one 32-key sub-tile at a time, straight into
+    // the E4M3 B operand.  Sub-tile `sub` of a row is one scale block of the
+    // second product (bytes 16·sub .. 16·sub + 15 of the row's two lanes; the
+    // lane of the lower half gives the scale of block 0, the upper one that of
+    // block 1): both lanes form the block's sum R alike (R = r_lo + r_hi) and
+    // take σ = frexp exponent of R − 8, so every element, at most R < 2^(σ+8),
+    // scales below 2^8; σ stays at least −126 so that 2^σ is a normal fp32
+    // number and 127 + σ a valid E8M0 code.  The lane's sum bounds each of its
+    // elements, so a sum at most 2^48 proves that no row outgrew m by more.
     float rs;
     auto exps = [&]() __attribute__((always_inline)) {
       const float mc = m * c;
-      float r2[2] = {0.f, 0.f};
+      int sig[T::NSUB];
+      float rsub[T::NSUB];
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {  // word w: bytes 4w .. 4w+3 = s[w/4][4(w%4) .. +3]
-        const int sub = w >> 2, r = 4 * (w & 3);
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[sub][r + 1], c, -mc));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(s[sub][r + 2], c, -mc));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(s[sub][r + 3], c, -mc));
-        r2[w & 1] += (e0 + e1) + (e2 + e3);
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, v, true);
+      for (int sub = 0; sub < T::NSUB; ++sub) {
+        float e[16], r2[2] = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) e[r + t] = __builtin_amdgcn_exp2f(fmaf(s[sub][r + t], c, -mc));
+          r2[(r >> 2) & 1] += (e[r] + e[r + 1]) + (e[r + 2] + e[r + 3]);
+        }
+        rsub[sub] = r2[0] + r2[1];
+        sig[sub] = max(__builtin_amdgcn_frexp_expf(pair_sum(rsub[sub])) - kPScaleLog2, -126);
+        const float sc = __uint_as_float((uint32_t)(sig[sub] + 127) << 23);  // 2^σ
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {  // word 4·sub + w4 of pb: bytes of s[sub][4·w4 .. 4·w4 + 3]
+          s16x2_t h = {0, 0};
+          h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, e[4 * w4], e[4 * w4 + 1], sc, false);
+          h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, e[4 * w4 + 2], e[4 * w4 + 3], sc, true);
+          pb[4 * sub + w4] = __builtin_bit_cast(int, h);
+        }
       }
-      rs = r2[0] + r2[1];
+      psc = kE8M0One + (g ? sig[1] : sig[0]);
+      rs = rsub[0] + rsub[1];
     };
     exps();
     if (__any(!(rs <= kFp8SumBound))) {  // also taken for inf / NaN sums (first tile: m = −∞)
@@ -301,7 +328,7 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
     s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop(kb, i), qf[kbk], s[sub], 0, 0, 0, kse, 0, qse);
   };
   auto pv_step = [&](const unsigned char* vb, int ds, int vse) __attribute__((always_inline)) {
-    acc[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop(vb, ds), pb, acc[ds], 0, 0, 0, vse, 0, kE8M0One);
+    acc[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop(vb, ds), pb, acc[ds], 0, 0, 0, vse, 0, psc);
   };
   constexpr int NQK = T::NSUB * T::KB;
   constexpr int NPV = T::DSUB;

@@ -119,21 +119,37 @@ def attention_fp8_ref(q, k, v, scale, causal, q_block=64, kv_block=64, rows=None
     return attention_ref(qh, kh, vh, scale, causal, rows=rows)
 
 
-def fp8_allowance(q, k, v, scale, causal, block=64, rows=None):
-    """The parity bound of the FP8 forward, per output row.
+def _block_mass(p, seen, av, pblock):
+    """Σ_i seen_i·P_b(i)·|v̂_i| per row, P_b the probability mass of the aligned
+    ``pblock``-key block that holds key i: p, seen [R, N], av [N, d] → [R, d]."""
+    R, N = p.shape
+    nb = -(-N // pblock)
+    pp = np.zeros((R, nb * pblock))
+    pp[:, :N] = p
+    mass = np.repeat(pp.reshape(R, nb, pblock).sum(axis=2), pblock, axis=1)[:, :N]
+    return (seen * mass) @ av
 
-    The kernel rounds each probability P̃_i = exp(s_i − m) (m at most the row's
-    true max, so P̃_i ≤ 2^8 is the only range it needs) to E4M3 before the second
-    product and divides by the fp32 sum ℓ of the unrounded P̃.  E4M3 rounding
-    moves a value by at most 2^−4 of itself (3 mantissa bits) or by 2^−10 (half
-    the subnormal spacing), whichever is larger; a later rescale by α ≤ 1 only
-    shrinks both.  With p_i = P̃_i/ℓ and ℓ ≥ ℓ* = Σ exp(s_i − max s):
 
-        |O − O_ref| ≤ 2^−4·Σ p_i |v̂_i| + 2^−10·Σ |v̂_i| / ℓ*
+def fp8_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=32):
+    """The schedule-free parity bound of the FP8 forward, per output element.
 
-    per element of O (v̂ the dequantised values of that column).  Returns
-    (O_ref, L_ref, allowance) as float64 [B, H, R, d], [B, H, R], [B, H, R, d]
-    for the query rows ``rows`` (all by default)."""
+    The kernel rounds each probability P̃_i = 2^(t_i − m) (m a reference max,
+    any stale value) to E4M3 before the second product, block-quantised like the
+    inputs: the P̃ of a row's aligned block of ``pblock`` keys are divided by a
+    power of two 2^σ no larger than 2^-7 times their sum R_b, rounded, and the
+    product is scaled back by 2^σ.  E4M3 rounding moves a value by at most 2^-4
+    of itself (3 mantissa bits) or by 2^-10 (half the subnormal spacing), so
+    P̃_i moves by at most 2^-4·P̃_i + 2^(σ−10) ≤ 2^-4·P̃_i + 2^-17·R_b.  The
+    kernel divides by the fp32 sum ℓ of the unrounded P̃, so with p_i = P̃_i/ℓ
+    (the exact softmax) and P_b = R_b/ℓ the block's probability mass:
+
+        |O − O_ref| ≤ 2^−4·Σ_i p_i |v̂_i| + 2^−17·(1 + 2^-10)·Σ_i P_b(i) |v̂_i|
+
+    over the keys the row sees (v̂ the dequantised values of that column; the
+    factor 1 + 2^-10 covers the fp32 rounding of the kernel's R_b).  Neither term
+    depends on the reference max or grows with N beyond the softmax weights.
+    Returns (O_ref, L_ref, allowance) as float64 [B, H, R, d], [B, H, R],
+    [B, H, R, d] for the query rows ``rows`` (all by default)."""
     from .ref import scores, safe_softmax
     qh = dequantize_blocks(*quantize_blocks(q, block), block)
     kh = dequantize_blocks(*quantize_blocks(k, block), block)
@@ -149,8 +165,9 @@ def fp8_allowance(q, k, v, scale, causal, block=64, rows=None):
             p, m, l = safe_softmax(s)
             o[b, h] = p @ vh[b, h]
             lse[b, h] = m + np.log(l)
-            seen = (p > 0).astype(np.float64)  # keys the row attends to (masked ones carry no rounding)
-            allow[b, h] = 2.0 ** -4 * (p @ np.abs(vh[b, h])) + 2.0 ** -10 * (seen @ np.abs(vh[b, h])) / l[:, None]
+            av = np.abs(vh[b, h])
+            seen = np.isfinite(s).astype(np.float64)  # keys the row attends to (masked ones carry no rounding)
+            allow[b, h] = 2.0 ** -4 * (p @ av) + 2.0 ** -17 * (1 + 2.0 ** -10) * _block_mass(p, seen, av, pblock)
     return o, lse, allow
 
 
@@ -158,21 +175,22 @@ def fp8_allowance(q, k, v, scale, causal, block=64, rows=None):
 #
 # attention_fp8_ref is the definition.  The FP8 forward reaches it up to two
 # things of its own: it rounds the probabilities P̃ to E4M3 before the second
-# product, against a reference maximum that it moves only now and then
-# (conditional rescaling, [cicada] §5, FlashAttention-4: the reference max of
-# a group of rows is moved only when some row of the group outgrows it by more
-# than 2^8, which keeps every P̃ below the format's 448); and both of its
+# product, block-quantised ([cicada] §4.4.1) against a reference maximum that
+# it moves only now and then (conditional rescaling, [cicada] §5,
+# FlashAttention-4: the reference max of a group of rows is moved only when
+# some row of the group outgrows it by more than 2^48); and both of its
 # products run on the FP8 matrix instruction, which does not sum exactly (see
 # mma_runs).  A bound that knows neither must allow every P̃ its worst
-# rounding (fp8_allowance) — and at long N that worst case outgrows O itself.
-# fp8_step_model carries the step out as described, in fp64, and so predicts
-# the kernel's output; what is left between the two is fp32 arithmetic,
-# bounded in fp8_step_allowance.
+# rounding (fp8_allowance).  fp8_step_model carries the step out as described,
+# in fp64, and so predicts the kernel's output; what is left between the two
+# is fp32 arithmetic, bounded in fp8_step_allowance.
 
 U_F32 = 2.0 ** -24            # unit roundoff of fp32
-FP8_RESCALE_LOG2 = 8.0        # growth of a row max (base-2 units) that moves the reference max
+FP8_RESCALE_LOG2 = 48.0       # growth of a row max (base-2 units) that moves the reference max
 FP8_GROUP_ROWS = 32           # query rows that share the decision to move it
 FP8_KEY_TILE = 64             # keys per step, in order
+FP8_P_BLOCK = 32              # keys of a row whose P̃ share one power-of-two scale
+FP8_P_SUM_LOG2 = 8            # a scaled P̃ block sums to less than 2^8
 EXP2_REL = 2.0 ** -21         # relative error allowed for the hardware exp2
 MMA_RUN = 8                   # reduction indices whose products share one alignment
 MMA_KEEP = 13                 # bits kept below a run's largest operand-exponent sum
@@ -245,7 +263,7 @@ def _groups_for(rows, N, group):
 
 
 def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mma_exact=False,
-                   group=FP8_GROUP_ROWS, tile=FP8_KEY_TILE, threshold=FP8_RESCALE_LOG2):
+                   group=FP8_GROUP_ROWS, tile=FP8_KEY_TILE, threshold=FP8_RESCALE_LOG2, pblock=FP8_P_BLOCK):
     """The FP8 forward's step, carried out in fp64 (a model, not the definition).
 
     Q, K, V are quantised block-wise (``quantize_blocks``, blocks of ``block``
@@ -260,9 +278,13 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
       (``group`` consecutive rows, aligned) has a tile max more than
       ``threshold`` above its M, every row of the group moves M to
       max(M, tile max) and multiplies ℓ and the accumulator by 2^(M_old − M);
-    * P̃ = 2^(t − M), rounded to E4M3 (``round_p``), enters the second product
-      by ``mma_runs`` with its keys in the order ``v_tile_key`` gives, times the
-      V tile's scale, added to the accumulator; ℓ sums the unrounded P̃;
+    * P̃ = 2^(t − M); ℓ sums it unrounded; for the second product the P̃ of each
+      row's aligned block of ``pblock`` keys are divided by 2^σ, σ = e − 8 with
+      e the frexp exponent of the block's sum (so the block's elements fall
+      below 2^8), σ ≥ −126, and rounded to E4M3 (``round_p``); the codes enter
+      the second product by ``mma_runs`` with their keys in the order
+      ``v_tile_key`` gives, each run times 2^σ of its block and the V tile's
+      scale, added to the accumulator;
     * O = acc / ℓ and L = M·ln 2 + ln ℓ.
 
     Besides the result, the model bounds how far a kernel doing the same with
@@ -274,12 +296,15 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
       boundary may round either way in the kernel; its largest possible change
       times |v̂|, plus — where the other rounding's product could reach its
       run's exponent and so move the run's grid — a grid step of every product
-      of the run, rescaled, over ℓ;
+      of the run, rescaled, over ℓ; where a block's sum lies within its error
+      bound of a power of two (the kernel's σ may be the other one), the larger
+      of the two choices' terms plus the difference of their products;
     * ``dev``: the fp32 additions of the second product's run sums and the
       accumulator (γ_9 of their magnitudes per tile) and the rescale products,
       carried through the tiles, over ℓ;
     * ``sched_amb``: a decision to move M within its error bound of the
-      threshold (the kernel may have taken the other branch).
+      threshold (the kernel may have taken the other branch), or a block sum
+      below 2^-100 (its P̃ may leave fp32's normal range).
     ``mma_exact``: exact matrix products (a kernel on exact matrix cores; the
     slip tests and the pin against the definition use it).
 
@@ -290,15 +315,15 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
     ``sched_amb`` (bool), and ``n_tiles``.
     """
     with np.errstate(divide="ignore", invalid="ignore"):  # rows past N give 0/0; they are dropped
-        return _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, tile, threshold)
+        return _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, tile, threshold, pblock)
 
 
-def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, tile, threshold):
+def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, tile, threshold, pblock):
     import torch
     q8, qs = quantize_blocks(q, block)
     k8, ks = quantize_blocks(k, block)
     v8, vs = quantize_blocks(v, block)
-    assert tile == block and tile % MMA_RUN == 0
+    assert tile == block and tile % MMA_RUN == 0 and tile % pblock == 0 and pblock % MMA_RUN == 0
     B, H, N, d = q8.shape
     assert d % 64 == 0
     c = scale * np.log2(np.e)
@@ -316,6 +341,7 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
     out["sched_amb"] = np.zeros((B, H, R), dtype=bool)
     rowidx = np.minimum(allrows, N - 1)
     slot = np.array([v_tile_key(j) for j in range(tile)])
+    run_blk = np.array([v_tile_key(MMA_RUN * r_) // pblock for r_ in range(tile // MMA_RUN)])  # block of each run
     sel = live.reshape(G, group)
     for b in range(B):
         for h in range(H):
@@ -331,6 +357,7 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
             exm = np.zeros((G, group))
             mov = np.zeros((G, group))
             samb = np.zeros(G, dtype=bool)
+            ramb = np.zeros((G, group), dtype=bool)   # a row whose block scale σ may differ
             for j in range(n_tiles):
                 k0, k1 = j * tile, min(N, (j + 1) * tile)
                 keys = np.arange(k0, k1)
@@ -377,23 +404,8 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                     mov += changed
                     m = mn
                 x = np.where(vis, np.exp2(t - m[:, :, None]), 0.0)
-                xr = e4m3_round(x) if round_p else x
                 ell += x.sum(axis=2)
-                # second product: P̃ in the slot order of the V tile, runs of 8 slots
                 nk = k1 - k0
-                xs = np.zeros((GR, tile))
-                vsl = np.zeros((tile, d))
-                ok = slot < nk
-                xs[:, ok] = xr.reshape(GR, nk)[:, slot[ok]]
-                vsl[ok] = v8[b, h][k0 + slot[ok]]
-                runs2, E2 = mma_runs(torch.from_numpy(xs), torch.from_numpy(vsl), exact=mma_exact)
-                sv = vs[b, h][j]
-                tcon = (runs2.sum(1).numpy() * sv).reshape(G, group, d)
-                tmag = (runs2.abs().sum(1).numpy() * sv).reshape(G, group, d)
-                dev = dev + g9 * (np.abs(acc) + dev + tmag)
-                acc = acc + tcon
-                vabs = np.abs(v8[b, h][k0:k1]) * sv
-                wab += np.maximum(x, np.abs(xr)) @ vabs
                 # how far the kernel's log2 P̃ may lie from this one
                 mfin = np.where(np.isfinite(m), m, 0.0)[:, :, None]
                 tv = np.where(vis, t, 0.0)
@@ -401,27 +413,85 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                       + EXP2_REL / np.log(2.0) + 2.0 ** -24)
                 ex = np.where(vis, ex, 0.0)
                 exm = np.maximum(exm, ex.max(axis=2))
-                if round_p:
-                    lo, hi = e4m3_round(x * np.exp2(-ex)), e4m3_round(x * np.exp2(ex))
-                    dx = np.maximum(hi - xr, xr - lo)
-                    if dx.any():
-                        dxs = np.zeros((GR, tile))
-                        dxs[:, ok] = dx.reshape(GR, nk)[:, slot[ok]]
-                        part = dxs @ (np.abs(vsl) * sv)
-                        if not mma_exact:
-                            # the other rounding may also move its run's exponent: when its product
-                            # could reach the run's exponent, allow every product of the run a grid
-                            # step at the larger of the two exponents
-                            alt = np.zeros((GR, tile))
-                            alt[:, ok] = np.maximum(np.abs(lo), np.abs(hi)).reshape(GR, nk)[:, slot[ok]]
-                            alt = np.where(dxs > 0, alt, 0.0)
-                            ea = e4m3_exponent(torch.from_numpy(alt))[:, :, None] + e4m3_exponent(torch.from_numpy(vsl))[None]
-                            ecand = ea.view(GR, tile // MMA_RUN, MMA_RUN, d).amax(2).numpy()
-                            e2 = E2.numpy()
-                            risky = (ecand >= e2) & (ecand > -1000)   # only runs that hold an ambiguous P̃
-                            step = np.ldexp(1.0, (np.maximum(e2, ecand) - MMA_KEEP).clip(-300, 300).astype(int)) * sv
-                            part = part + MMA_RUN * np.where(risky, step, 0.0).sum(axis=1)
-                        amb += part.reshape(G, group, d)
+                # P̃ block-quantised per row and aligned pblock-key block: σ = (frexp
+                # exponent of the block's sum) − 8, at least −126; codes x/2^σ in E4M3
+                nb = tile // pblock
+                xp = np.zeros((G, group, tile))
+                xp[..., :nk] = x
+                rb = xp.reshape(G, group, nb, pblock).sum(axis=3)
+                sig = np.maximum(np.frexp(rb)[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
+                # the kernel's fp32 sum lies within a factor 1 ± δ of rb: σ may differ
+                # where that interval holds a power of two, or where the block's P̃
+                # leave fp32's normal range (the kernel's exp2 may flush them)
+                exb = np.zeros((G, group, tile))
+                exb[..., :nk] = ex
+                dl = np.expm1(exb.reshape(G, group, nb, pblock).max(axis=3) * np.log(2.0)) + _gamma(pblock)
+                s_lo = np.maximum(np.frexp(rb * (1 - dl))[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
+                s_hi = np.maximum(np.frexp(rb * (1 + dl))[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
+                ramb |= np.any((rb > 0) & (rb < 2.0 ** -100), axis=2)
+                ok = slot < nk
+                sv = vs[b, h][j]
+                vsl = np.zeros((tile, d))
+                vsl[ok] = v8[b, h][k0 + slot[ok]]
+
+                def second(sg):
+                    """The second product's runs for block exponents sg: codes, runs
+                    (each times 2^σ of its block) [GR, tile/8, d], their grids' exponents,
+                    2^σ per key and per run."""
+                    sk_ = np.exp2(np.repeat(sg, pblock, axis=2)[..., :nk])
+                    xc_ = e4m3_round(x / sk_) if round_p else x / sk_
+                    xs_ = np.zeros((GR, tile))
+                    xs_[:, ok] = xc_.reshape(GR, nk)[:, slot[ok]]
+                    runs_, E_ = mma_runs(torch.from_numpy(xs_), torch.from_numpy(vsl), exact=mma_exact)
+                    rsc_ = np.exp2(sg.reshape(GR, nb))[:, run_blk]
+                    return xc_, runs_.numpy() * rsc_[:, :, None], E_, sk_, rsc_
+
+                def ambiguous_part(xc_, E_, sk_, rsc_):
+                    """A bound on how far the second product can move when each P̃
+                    lies within 2^(±ex) of x: roundings that may go the other way,
+                    and the run grids they may move."""
+                    xq = x / sk_
+                    lo, hi = e4m3_round(xq * np.exp2(-ex)), e4m3_round(xq * np.exp2(ex))
+                    dx = np.maximum(hi - xc_, xc_ - lo)                          # in code units
+                    if not dx.any():
+                        return 0.0
+                    dxs = np.zeros((GR, tile))
+                    dxs[:, ok] = (dx * sk_).reshape(GR, nk)[:, slot[ok]]
+                    part = dxs @ (np.abs(vsl) * sv)
+                    if not mma_exact:
+                        # the other rounding may also move its run's exponent: when its product
+                        # could reach the run's exponent, allow every product of the run a grid
+                        # step at the larger of the two exponents
+                        alt = np.zeros((GR, tile))
+                        alt[:, ok] = np.maximum(np.abs(lo), np.abs(hi)).reshape(GR, nk)[:, slot[ok]]
+                        alt = np.where(dxs > 0, alt, 0.0)
+                        ea = e4m3_exponent(torch.from_numpy(alt))[:, :, None] + e4m3_exponent(torch.from_numpy(vsl))[None]
+                        ecand = ea.view(GR, tile // MMA_RUN, MMA_RUN, d).amax(2).numpy()
+                        e2 = E_.numpy()
+                        risky = (ecand >= e2) & (ecand > -1000)   # only runs that hold an ambiguous P̃
+                        step = np.ldexp(1.0, (np.maximum(e2, ecand) - MMA_KEEP).clip(-300, 300).astype(int))
+                        part = part + MMA_RUN * np.where(risky, step * rsc_[:, :, None] * sv, 0.0).sum(axis=1)
+                    return part
+
+                xc, r2, E2, sk, rsc = second(sig)
+                xr = xc * sk
+                tcon = (r2.sum(1) * sv).reshape(G, group, d)
+                tmag = (np.abs(r2).sum(1) * sv).reshape(G, group, d)
+                dev = dev + g9 * (np.abs(acc) + dev + tmag)
+                acc = acc + tcon
+                vabs = np.abs(v8[b, h][k0:k1]) * sv
+                wab += np.maximum(x, np.abs(xr)) @ vabs
+                part = ambiguous_part(xc, E2, sk, rsc) if round_p else 0.0
+                flip = (s_lo != s_hi) & (rb > 0)
+                if flip.any():
+                    # the kernel's σ may be the other one: its runs, and the roundings
+                    # around them, bound what it may add beyond the model's
+                    sig2 = np.where(flip, np.where(s_lo != sig, s_lo, s_hi), sig)
+                    xc2, r22, E22, sk2, rsc2 = second(sig2)
+                    part2 = ambiguous_part(xc2, E22, sk2, rsc2) if round_p else 0.0
+                    part = np.maximum(part, part2) + (np.abs(r22 - r2).sum(1) * sv)
+                if np.any(part):
+                    amb += np.broadcast_to(part, (GR, d)).reshape(G, group, d)
             o = acc / ell[:, :, None]
             out["o"][b, h] = o[sel]
             out["wabs"][b, h] = (wab / ell[:, :, None])[sel]
@@ -430,7 +500,7 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
             out["lse"][b, h] = (m * np.log(2.0) + np.log(ell))[sel]
             out["ex_max"][b, h] = exm[sel]
             out["moves"][b, h] = mov[sel]
-            out["sched_amb"][b, h] = np.broadcast_to(samb[:, None], (G, group))[sel]
+            out["sched_amb"][b, h] = (np.broadcast_to(samb[:, None], (G, group)) | ramb)[sel]
     out["rows"] = allrows[live]
     out["n_tiles"] = n_tiles
     return out
@@ -470,15 +540,16 @@ def _logit_trunc_bound(q8, qs, k8, ks, rows, block):
     return t * qs[rows // block][:, None] * np.repeat(ks, block)[:k8.shape[0]][None, :]
 
 
-def fp8_mma_allowance(q, k, v, scale, causal, block=64, rows=None):
+def fp8_mma_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=FP8_P_BLOCK):
     """Schedule-free bounds on how far the matrix instruction's truncation
     (mma_runs) can move O and L away from exact attention of the dequantised
     inputs.
 
     A truncated product loses less than one grid step 2^(E − 13) ≤ 2^-13 times the
     largest product of its run, so a run of 8 loses less than 2^-10 of the sum
-    of its |products|.  Second product: |ΔO| ≤ 2^-10·Σ_j w_j|v̂_j| / ℓ with
-    w_j ≤ (1 + 2^-4)·P̃_j + 2^-10 (the rounded weight).  First product: logit j
+    of its |products| (a power-of-two operand scale scales both alike).  Second
+    product: |ΔO| ≤ 2^-10·Σ_j w_j|v̂_j| / ℓ with w_j/ℓ ≤ (1 + 2^-4)·p_j +
+    2^-17·(1 + 2^-10)·P_b(j) (the rounded weight, as in fp8_allowance).  First product: logit j
     moves by less than T_j (``_logit_trunc_bound``, times the scale), which
     moves each weight by a factor within e^(±T_j): O by at most
     Σ_j p_j·(e^(2T_j) − 1)·(|v̂_j| + |O|) (numerator and ℓ), and
@@ -499,8 +570,9 @@ def fp8_mma_allowance(q, k, v, scale, causal, block=64, rows=None):
             p, _, l = safe_softmax(s)
             o = p @ vh[b, h]
             av = np.abs(vh[b, h])
-            seen = (p > 0).astype(np.float64)
-            pv = 2.0 ** -10 * ((1 + 2.0 ** -4) * (p @ av) + 2.0 ** -10 * (seen @ av) / l[:, None])
+            seen = np.isfinite(s).astype(np.float64)
+            pv = 2.0 ** -10 * ((1 + 2.0 ** -4) * (p @ av)
+                               + 2.0 ** -17 * (1 + 2.0 ** -10) * _block_mass(p, seen, av, pblock))
             tb = np.where(p > 0, scale * _logit_trunc_bound(q8[b, h], qs[b, h], k8[b, h], ks[b, h], rows, block), 0.0)
             qk = (p * np.expm1(2 * tb)) @ av + (p * np.expm1(2 * tb)).sum(axis=1)[:, None] * np.abs(o)
             out[b, h] = pv + qk

@@ -143,10 +143,25 @@ def test_fp8_attention_moves_away_from_exact_attention_by_the_rounding():
     assert 0 < np.abs(o - ro).max() < 0.25 and np.abs(l - rl).max() < 0.5
 
 
+def _round_p_blocks(pt, pblock=32):
+    """P̃ [R, N] rounded as the FP8 forward rounds it for its second product, in
+    plain NumPy: each aligned block of ``pblock`` keys of a row is divided by the
+    power of two 2^σ, σ = e − 8 with 2^(e−1) ≤ block sum < 2^e (at least −126),
+    rounded to E4M3 and multiplied back."""
+    R, N = pt.shape
+    nb = -(-N // pblock)
+    padded = np.zeros((R, nb * pblock))
+    padded[:, :N] = pt
+    sums = padded.reshape(R, nb, pblock).sum(axis=2)
+    e = np.where(sums > 0, np.floor(np.log2(np.where(sums > 0, sums, 1.0))) + 1, 0)
+    sk = np.repeat(2.0 ** np.maximum(e - 8, -126), pblock, axis=1)[:, :N]
+    return e4m3_round(pt / sk) * sk
+
+
 def _sim_kernel(q, k, v, scale, causal, shift, rng):
     """The FP8 forward's arithmetic on the CPU: P̃ against a reference max below
-    the true one by up to `shift` (in natural-log units), rounded to E4M3 for the
-    second product, O divided by the sum of the unrounded P̃."""
+    the true one by up to `shift` (in natural-log units), block-quantised for the
+    second product (_round_p_blocks), O divided by the sum of the unrounded P̃."""
     from oracle.fp8 import dequantize_blocks, quantize_blocks
     from oracle.ref import scores
     qh, kh, vh = (dequantize_blocks(*quantize_blocks(t, 64), 64) for t in (q, k, v))
@@ -156,13 +171,14 @@ def _sim_kernel(q, k, v, scale, causal, shift, rng):
             s = scores(qh[b, h], kh[b, h], scale, causal)
             m = s.max(axis=1) - rng.uniform(0, shift, s.shape[0])
             pt = np.exp(s - m[:, None])
-            o[b, h] = (e4m3_round(pt) @ vh[b, h]) / pt.sum(axis=1)[:, None]
+            o[b, h] = (_round_p_blocks(pt) @ vh[b, h]) / pt.sum(axis=1)[:, None]
     return o
 
 
 def test_fp8_allowance_covers_the_kernel_arithmetic():
-    """Random stale maxima up to the rescale threshold (2^8) and E4M3 weights:
-    the simulated kernel output stays within the bound on every element."""
+    """Random stale maxima up to the rescale threshold (2^48) and block-quantised
+    E4M3 weights: the simulated kernel output stays within the bound on every
+    element."""
     from oracle.fp8 import fp8_allowance
     rng = np.random.default_rng(17)
     shape = (1, 2, 200, 128)
@@ -172,10 +188,25 @@ def test_fp8_allowance_covers_the_kernel_arithmetic():
     k[:, :, ::37] *= 6.0  # a few dominant keys: weights near 1 next to many subnormal ones
     for causal in (False, True):
         ro, rl, allow = fp8_allowance(q, k, v, 0.125, causal)
-        for shift in (0.0, 8 * np.log(2)):
+        for shift in (0.0, 8 * np.log(2), 48 * np.log(2)):
             o = _sim_kernel(q, k, v, 0.125, causal, shift, rng)
             err = np.abs(o - ro)
             assert np.all(err <= allow * (1 + 1e-9)), (causal, shift, float((err / allow).max()))
+
+
+def test_round_p_blocks_pins():
+    """The block rounding on hand-made rows: a block summing to 1 is scaled by
+    2^-7 (its elements become codes below 2^7); 0.3 + 0.3 in one block (sum 0.6,
+    σ = −8) both become 0.3·256 = 76.8 → 80 → 0.3125; a lone weight 2^-40 is
+    exact (its block takes σ = −47); an all-zero block stays zero."""
+    pt = np.zeros((3, 64))
+    pt[0, 0] = 1.0
+    pt[1, 0] = pt[1, 1] = 0.3
+    pt[2, 40] = 2.0 ** -40
+    r = _round_p_blocks(pt)
+    assert r[0, 0] == 1.0 and r[2, 40] == 2.0 ** -40
+    assert r[1, 0] == r[1, 1] == 0.3125
+    assert not r[:, 2:40].any() and not r[0, 1:].any()
 
 
 # ---- the kernel-step model and the tight FP8 contract ---------------------------------
@@ -192,22 +223,24 @@ LN2 = float(np.log(2.0))
 @pytest.mark.parametrize("N", [1, 65, 300])
 def test_step_model_without_rounding_is_the_definition(N, causal):
     """With P̃ left unrounded and exact matrix products, the model's reference-max
-    schedule changes nothing in exact arithmetic ([cicada] §5: ℓ and the
-    accumulator share the stale max): O and L equal exact attention of the
-    dequantised inputs."""
+    schedule and the block scales of P̃ change nothing in exact arithmetic
+    ([cicada] §5: ℓ and the accumulator share the stale max): O and L equal
+    exact attention of the dequantised inputs."""
     w = synth.WORKLOADS[2].with_(B=1, H=2, N=N, causal=causal, boost_frac=0.03, wid=900 + N + causal)
     q, k, v = synth.make_prefill(w)
-    m = fp8_step_model(q, k, v, w.scale, causal, round_p=False, mma_exact=True)
+    # a low threshold, so that the boosted keys move the reference max
+    m = fp8_step_model(q, k, v, w.scale, causal, round_p=False, mma_exact=True, threshold=4.0)
     o, l = attention_fp8_ref(q, k, v, w.scale, causal)
     assert np.allclose(m["o"], o, rtol=1e-12, atol=1e-13) and np.allclose(m["lse"], l, rtol=1e-13, atol=1e-12)
     if N >= 300:
         assert m["moves"].max() >= 2  # the boosted keys did move the reference max
 
 
-def _integer_logit_inputs(N, grow_at=None, grow_row=0, grow=9.0, base=3.0):
+def _integer_logit_inputs(N, grow_at=None, grow_row=0, grow=51.0, base=3.0):
     """q̂, k̂ for scale = ln 2 (so the base-2 logits are t = q̂·k̂): t_ij = −(j mod 3);
     from key ``grow_at`` on every row's logits are ``base`` higher, and those of
-    row ``grow_row`` ``grow`` higher."""
+    row ``grow_row`` ``grow`` higher (grow − base must stay an E4M3 value after
+    the K block's scale: 48 with base 3, and 40, 44, 48, 52 with base 4 do)."""
     d = 128
     q = np.zeros((1, 1, N, d))
     k = np.zeros((1, 1, N, d))
@@ -223,12 +256,12 @@ def _integer_logit_inputs(N, grow_at=None, grow_row=0, grow=9.0, base=3.0):
 
 
 def test_step_model_is_exact_on_representable_weights():
-    """Logits that are integers in base 2 make every P̃ an exact power of two
-    between 2^-2 and 2^8 (the stale max), all of them E4M3 values: rounding
-    changes nothing, and with exact matrix products the model equals the
-    definition, although the keys at +9 (row 250) move the reference max of
-    the row's whole group while the next group, whose rows grow by 3 only,
-    keeps its stale max."""
+    """Logits that are integers in base 2 make every P̃ an exact power of two, and
+    so every block-scaled code (a power of two between 2^-2 and 2^7 times the
+    block's largest): rounding changes nothing, and with exact matrix products
+    the model equals the definition, although the keys at +51 (row 250) move the
+    reference max of the row's whole group while the next group, whose rows grow
+    by 3 only, keeps its stale max."""
     q, k, v = _integer_logit_inputs(300, grow_at=192, grow_row=250)
     for causal in (False, True):
         m = fp8_step_model(q, k, v, LN2, causal, mma_exact=True)
@@ -242,13 +275,13 @@ def test_step_model_is_exact_on_representable_weights():
 
 def test_step_model_schedule():
     """The reference max of a 32-row group moves for every row of the group when
-    one row outgrows it by more than 2^8 (growths 9 and 8.5, E4M3-exact after
-    quantisation), not at 7.5, and a growth within the fp32 error bound of the
-    threshold (8 exactly, nudged either way by the scale) is flagged."""
-    cases = [(9.0, 1.0, 2, False), (8.5, 1.0, 2, False), (7.5, 1.0, 1, False),
-             (8.0, 1.0 + 1e-9, 2, True), (8.0, 1.0 - 1e-9, 1, True), (8.0, 1.0, 1, True)]
+    one row outgrows it by more than 2^48 (growths 56 and 52, E4M3-exact after
+    quantisation), not at 44, and a growth within the fp32 error bound of the
+    threshold (48 exactly, nudged either way by the scale) is flagged."""
+    cases = [(56.0, 1.0, 2, False), (52.0, 1.0, 2, False), (44.0, 1.0, 1, False),
+             (48.0, 1.0 + 1e-9, 2, True), (48.0, 1.0 - 1e-9, 1, True), (48.0, 1.0, 1, True)]
     for grow, f, moves, amb in cases:
-        q, k, v = _integer_logit_inputs(300, grow_at=128, grow_row=3, grow=grow)
+        q, k, v = _integer_logit_inputs(300, grow_at=128, grow_row=3, grow=grow, base=4.0)
         m = fp8_step_model(q, k, v, LN2 * f, False)
         assert np.all(m["moves"][0, 0, :32] == moves), (grow, f)  # the whole group of row 3
         assert np.all(m["moves"][0, 0, 32:] == 1), (grow, f)      # other groups: only the first tile
@@ -322,12 +355,14 @@ def test_v_tile_key_is_a_permutation():
     assert keys[:8] == [0, 1, 2, 3, 8, 9, 10, 11] and keys[32:36] == [4, 5, 6, 7]
 
 
-def _instr_f32(a, b, acc):
+def _instr_f32(a, b, acc, run_scale=None):
     """One FP8 matrix instruction in float32, written apart from the oracle's
     mma_runs: for each run of 8 reduction indices the products, each cut toward
     zero to the grid 2^(E−13) of the run's largest exponent sum, are summed (the
-    sum is exact in fp32); the eight run sums are then added to ``acc`` one by
-    one in float32.  a [R, 64], b [64, C], acc [R, C] float32 tensors."""
+    sum is exact in fp32) and times the run's power-of-two operand scale
+    (``run_scale`` [R, 8], 1 by default); the eight run sums are then added to
+    ``acc`` one by one in float32.  a [R, 64], b [64, C], acc [R, C] float32
+    tensors."""
     R, C = a.shape[0], b.shape[1]
     ea = torch.where(a != 0, torch.frexp(a)[1].float() - 1, torch.full_like(a, -1e4)).clamp(min=-6)
     eb = torch.where(b != 0, torch.frexp(b)[1].float() - 1, torch.full_like(b, -1e4)).clamp(min=-6)
@@ -336,24 +371,27 @@ def _instr_f32(a, b, acc):
         e = torch.where(p != 0, ea[:, 8 * g:8 * g + 8, None] + eb[None, 8 * g:8 * g + 8, :],
                         torch.full_like(p, -1e4))
         grid = torch.exp2((e.amax(1) - 13).clamp(min=-126))[:, None, :]
-        acc = acc + (torch.trunc(p / grid) * grid).sum(1)
+        run = (torch.trunc(p / grid) * grid).sum(1)
+        acc = acc + (run if run_scale is None else run * run_scale[:, g:g + 1])
     return acc
 
 
 def _sim_fp32_kernel(q, k, v, scale, causal, rows):
     """A float32 re-enactment of the FP8 forward's arithmetic, written apart from
     the model: logits from two float32 matrix instructions on the E4M3 codes times
-    the block scales, exp2 and sums in float32, P̃ rounded to E4M3 by torch's
-    float8_e4m3fn conversion, the second product by the instruction on the keys
-    in the V tile order, the reference max of each 32-row group moved when one of
-    its rows outgrows it by more than 2^8, O = acc·(1/ℓ) rounded to bf16,
-    L = m·scale + ln ℓ.  Returns (O, L) on the rows of every 32-row group that
-    holds one of ``rows``."""
+    the block scales, exp2 and sums in float32, the reference max of each 32-row
+    group moved when one of its rows outgrows it by more than 2^48, P̃ of each
+    row's 32-key half tile divided by 2^σ (σ from the float32 sum of the half)
+    and rounded to E4M3 by torch's float8_e4m3fn conversion, the second product
+    by the instruction on the keys in the V tile order with each run scaled by
+    its half's 2^σ, O = acc·(1/ℓ) rounded to bf16, L = m·scale + ln ℓ.  Returns
+    (O, L) on the rows of every 32-row group that holds one of ``rows``."""
     from oracle.fp8 import quantize_blocks
     (q8, qs), (k8, ks), (v8, vs) = (quantize_blocks(t, 64) for t in (q, k, v))
     B, H, N, d = q8.shape
     c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
     order = [32 * ((j >> 4) & 1) + 8 * ((j & 15) >> 2) + 4 * (j >> 5) + (j & 3) for j in range(64)]
+    run_half = [order[8 * g] // 32 for g in range(8)]  # the 32-key half tile each run of 8 slots holds
     groups = np.unique(np.asarray(rows) // 32)
     outs_o, outs_l = [], []
     f = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
@@ -385,7 +423,7 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows):
                     mt = s.max(axis=1)
                     with np.errstate(invalid="ignore"):
                         grow = (mt - m) * c
-                    if np.any(grow > np.float32(8.0)):
+                    if np.any(grow > np.float32(48.0)):
                         mn = np.fmax(m, mt)
                         with np.errstate(invalid="ignore"):
                             al = np.exp2((m - mn) * c).astype(np.float32)
@@ -394,10 +432,15 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows):
                     with np.errstate(invalid="ignore"):
                         x = np.exp2(s * c - (m * c)[:, None]).astype(np.float32)
                     x = np.where(np.isfinite(s), x, np.float32(0))
-                    x8 = torch.from_numpy(x).to(torch.float8_e4m3fn).float()
+                    half_sum = np.stack([x[:, :32].sum(axis=1, dtype=np.float32),
+                                         x[:, 32:].sum(axis=1, dtype=np.float32)], axis=1)
+                    sig = np.maximum(np.frexp(half_sum)[1] - 8, -126)
+                    sc = np.ldexp(np.float32(1), sig).astype(np.float32)          # [rows, 2]
+                    x8 = torch.from_numpy(x / np.repeat(sc, 32, axis=1)).to(torch.float8_e4m3fn).float()
                     vt = np.zeros((64, d), np.float32)
                     vt[:min(64, N - j)] = v8[b, h][j:j + 64]
-                    acc = _instr_f32(x8[:, order], f(vt[order] * np.float32(vs[b, h][j // 64])), acc)
+                    acc = _instr_f32(x8[:, order], f(vt[order] * np.float32(vs[b, h][j // 64])), acc,
+                                     run_scale=torch.from_numpy(sc[:, run_half]))
                     ell = (ell + x.sum(axis=1, dtype=np.float32)).astype(np.float32)
                 o[b, h] = (acc * torch.from_numpy(np.float32(1) / ell)[:, None]).numpy()
                 lse[b, h] = m * np.float32(scale) + np.log(ell)
