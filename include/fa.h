@@ -279,8 +279,11 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
  * fa_fwd_fp8 computes O [B, H, N, d] (bf16) and L [B, H, N] (fp32) of the
  * attention these operands define, exact attention of the dequantised
  * Q̂ = s·q₈, K̂, V̂ with scale and causal as for fa_fwd, except that the
- * probabilities enter the second product rounded to E4M3 (O is divided by the
- * sum of the unrounded ones).  Both products run on the FP8 matrix cores with
+ * probabilities enter the second product rounded to E4M3, block-quantised in
+ * turn: the probabilities of a row over each aligned half (32 keys) of a
+ * 64-key tile are divided by a power of two 2^σ no larger than 2^-7 times their
+ * sum before rounding, and the product is scaled back by 2^σ (O is divided by
+ * the sum of the unrounded ones).  Both products run on the FP8 matrix cores with
  * the block scales applied inside them.  All pointers are device pointers the
  * caller owns; packed_bytes is the size of the packed buffer, which must be
  * at least fa_fp8_packed_bytes(B, H, N, d) and hold what fa_quantize_fp8 wrote
