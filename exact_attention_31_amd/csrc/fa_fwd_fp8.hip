@@ -239,6 +239,7 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   f32x16_t s[T::NSUB];
   i32x8_t pb;      // 2^-σ P̃ of the tile in E4M3, the B operand of the second product
   int psc = kE8M0One;  // E8M0 scale 127 + σ of this lane's block of pb (see below)
+  float pe[T::NSUB][16], rsub[T::NSUB];  // P̃ of the tile in fp32 and the lane's sums per sub-tile
 
   auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
     const int kv0 = j * T::BN;
@@ -252,41 +253,24 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
           if (key > lim) s[sub][r] = -INFINITY;
         }
     }
-    // P̃ against the reference max, one 32-key sub-tile at a time, straight into
-    // the E4M3 B operand.  Sub-tile `sub` of a row is one scale block of the
-    // second product (bytes 16·sub .. 16·sub + 15 of the row's two lanes; the
-    // lane of the lower half gives the scale of block 0, the upper one that of
-    // block 1): both lanes form the block's sum R alike (R = r_lo + r_hi) and
-    // take σ = frexp exponent of R − 8, so every element, at most R < 2^(σ+8),
-    // scales below 2^8; σ stays at least −126 so that 2^σ is a normal fp32
-    // number and 127 + σ a valid E8M0 code.  The lane's sum bounds each of its
-    // elements, so a sum at most 2^48 proves that no row outgrew m by more.
+    // P̃ against the reference max in fp32, and the lane's sum over each 32-key
+    // sub-tile (the E4M3 conversion follows in the matrix phase, `convert`).
+    // The lane's sum bounds each of its elements, so a sum at most 2^48 proves
+    // that no row outgrew m by more.
     float rs;
     auto exps = [&]() __attribute__((always_inline)) {
       const float mc = m * c;
-      int sig[T::NSUB];
-      float rsub[T::NSUB];
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub) {
-        float e[16], r2[2] = {0.f, 0.f};
+        float r2[2] = {0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) e[r + t] = __builtin_amdgcn_exp2f(fmaf(s[sub][r + t], c, -mc));
-          r2[(r >> 2) & 1] += (e[r] + e[r + 1]) + (e[r + 2] + e[r + 3]);
+          for (int t = 0; t < 4; ++t) pe[sub][r + t] = __builtin_amdgcn_exp2f(fmaf(s[sub][r + t], c, -mc));
+          r2[(r >> 2) & 1] += (pe[sub][r] + pe[sub][r + 1]) + (pe[sub][r + 2] + pe[sub][r + 3]);
         }
         rsub[sub] = r2[0] + r2[1];
-        sig[sub] = max(__builtin_amdgcn_frexp_expf(pair_sum(rsub[sub])) - kPScaleLog2, -126);
-        const float sc = __uint_as_float((uint32_t)(sig[sub] + 127) << 23);  // 2^σ
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {  // word 4·sub + w4 of pb: bytes of s[sub][4·w4 .. 4·w4 + 3]
-          s16x2_t h = {0, 0};
-          h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, e[4 * w4], e[4 * w4 + 1], sc, false);
-          h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, e[4 * w4 + 2], e[4 * w4 + 3], sc, true);
-          pb[4 * sub + w4] = __builtin_bit_cast(int, h);
-        }
       }
-      psc = kE8M0One + (g ? sig[1] : sig[0]);
       rs = rsub[0] + rsub[1];
     };
     exps();
@@ -330,10 +314,34 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   auto pv_step = [&](const unsigned char* vb, int ds, int vse) __attribute__((always_inline)) {
     acc[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop(vb, ds), pb, acc[ds], 0, 0, 0, vse, 0, psc);
   };
+  // P̃ of the tile into the E4M3 B operand, a quarter (two words) per call, so
+  // that the matrix phase can issue it between the MFMAs of the first product.
+  // Sub-tile `sub` of a row is one scale block of the second product (bytes
+  // 16·sub .. 16·sub + 15 of the row's two lanes; the lane of the lower half
+  // gives the scale of block 0, the upper one that of block 1): both lanes form
+  // the block's sum R alike (R = r_lo + r_hi) and take σ = frexp exponent of
+  // R − 8, so every element, at most R < 2^(σ+8), scales below 2^8; σ stays at
+  // least −126 so that 2^σ is a normal fp32 number and 127 + σ a valid E8M0 code.
+  int sig[T::NSUB];
+  auto convert = [&](int part) __attribute__((always_inline)) {  // part 0..3: words 2·part, 2·part + 1
+    const int sub = part >> 1;
+    if ((part & 1) == 0) sig[sub] = max(__builtin_amdgcn_frexp_expf(pair_sum(rsub[sub])) - kPScaleLog2, -126);
+    const float sc = __uint_as_float((uint32_t)(sig[sub] + 127) << 23);  // 2^σ
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int w4 = 2 * (part & 1) + h;
+      s16x2_t x = {0, 0};
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, pe[sub][4 * w4], pe[sub][4 * w4 + 1], sc, false);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, pe[sub][4 * w4 + 2], pe[sub][4 * w4 + 3], sc, true);
+      pb[4 * sub + w4] = __builtin_bit_cast(int, x);
+    }
+    if (part == 3) psc = kE8M0One + (g ? sig[1] : sig[0]);
+  };
   constexpr int NQK = T::NSUB * T::KB;
   constexpr int NPV = T::DSUB;
   static_assert(NQK == NPV, "interleave pairs one MFMA of each product");
-  // matrix phase X(j): Oᵀ += Vᵀ_j P̃ᵀ_j (if do_pv) and Sᵀ_{j+1} = K_{j+1} Qᵀ (if do_qk)
+  // matrix phase X(j): Sᵀ_{j+1} = K_{j+1} Qᵀ (if do_qk) with P̃_j's conversion issued
+  // between its MFMAs, then Oᵀ += Vᵀ_j P̃ᵀ_j (if do_pv)
   auto matrix = [&](const unsigned char* vb, const unsigned char* kb, bool do_pv, bool do_qk, int vse, int kse)
       __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
@@ -344,8 +352,11 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (do_qk) qk_step(kb, i, kse);
-      if (do_pv) pv_step(vb, i, vse);
+      if (do_pv) convert(i);
     }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i)
+      if (do_pv) pv_step(vb, i, vse);
     __builtin_amdgcn_s_setprio(0);
   };
 
