@@ -262,12 +262,13 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
       const float mc = m * c;
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub) {
-        float r2[2] = {0.f, 0.f};
+        float r2[2];
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) pe[sub][r + t] = __builtin_amdgcn_exp2f(fmaf(s[sub][r + t], c, -mc));
-          r2[(r >> 2) & 1] += (pe[sub][r] + pe[sub][r + 1]) + (pe[sub][r + 2] + pe[sub][r + 3]);
+          const float q4 = (pe[sub][r] + pe[sub][r + 1]) + (pe[sub][r + 2] + pe[sub][r + 3]);
+          r2[(r >> 2) & 1] = r < 8 ? q4 : r2[(r >> 2) & 1] + q4;
         }
         rsub[sub] = r2[0] + r2[1];
       }
