@@ -315,7 +315,9 @@ def sample_gfx_clock(run, seconds=1.0):
 def time_prefill_workloads(torch, fa, synth, dev, args):
     """Every prefill workload on its own, each call between HIP events: warm (the
     calls back to back, inputs in the caches where they fit) and cold (a 512 MB
-    buffer written between calls, outside the timed region)."""
+    buffer written between calls, outside the timed region); and warm_graph, the
+    K calls captured in one HIP graph and timed as one replay (for short calls
+    the per-call events also hold the host's launch work)."""
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     res = {}
     for w in synth.WORKLOADS[:4]:
@@ -341,14 +343,30 @@ def time_prefill_workloads(torch, fa, synth, dev, args):
             e[1].record()
         torch.cuda.synchronize()
         cold = [e[0].elapsed_time(e[1]) for e in ev]
+        # the same K calls captured once in a HIP graph and replayed between two events:
+        # no host work between the calls, so short calls are not timed with their launch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        replay = g0.elapsed_time(g1) / args.steps
+        del graph
         flops = synth.prefill_flops(w)
         ent = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "algorithmic_flops": flops,
                "algorithmic_bytes": synth.prefill_bytes(w)}
-        for label, ms in (("warm", warm), ("cold", cold)):
+        for label, ms in (("warm", warm), ("cold", cold), ("warm_graph", [replay])):
             avg = sum(ms) / len(ms)
             tf = flops / (avg * 1e-3) / 1e12
             ent[label] = {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "tflops": round(tf, 2),
                           "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        ent["warm_graph"]["note"] = f"{args.steps} calls replayed from one HIP graph, timed as one replay"
         if w.N * w.H * w.B <= 256:
             ent["note"] = "one workgroup: launch-latency bound, no roofline claim"
         res[w.name] = ent
