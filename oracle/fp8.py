@@ -298,13 +298,14 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
       run's exponent and so move the run's grid — a grid step of every product
       of the run, rescaled, over ℓ; where a block's sum lies within its error
       bound of a power of two (the kernel's σ may be the other one), the larger
-      of the two choices' terms plus the difference of their products;
+      of the two choices' terms plus the difference of their products; a block
+      whose sum is below 2^-100 (its P̃ may leave fp32's normal range in the
+      kernel), 2.125 times its whole contribution Σ P̃·|v̂|;
     * ``dev``: the fp32 additions of the second product's run sums and the
       accumulator (γ_9 of their magnitudes per tile) and the rescale products,
       carried through the tiles, over ℓ;
     * ``sched_amb``: a decision to move M within its error bound of the
-      threshold (the kernel may have taken the other branch), or a block sum
-      below 2^-100 (its P̃ may leave fp32's normal range).
+      threshold (the kernel may have taken the other branch).
     ``mma_exact``: exact matrix products (a kernel on exact matrix cores; the
     slip tests and the pin against the definition use it).
 
@@ -357,7 +358,6 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
             exm = np.zeros((G, group))
             mov = np.zeros((G, group))
             samb = np.zeros(G, dtype=bool)
-            ramb = np.zeros((G, group), dtype=bool)   # a row whose block scale σ may differ
             for j in range(n_tiles):
                 k0, k1 = j * tile, min(N, (j + 1) * tile)
                 keys = np.arange(k0, k1)
@@ -421,14 +421,15 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                 rb = xp.reshape(G, group, nb, pblock).sum(axis=3)
                 sig = np.maximum(np.frexp(rb)[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
                 # the kernel's fp32 sum lies within a factor 1 ± δ of rb: σ may differ
-                # where that interval holds a power of two, or where the block's P̃
-                # leave fp32's normal range (the kernel's exp2 may flush them)
+                # where that interval holds a power of two
                 exb = np.zeros((G, group, tile))
                 exb[..., :nk] = ex
                 dl = np.expm1(exb.reshape(G, group, nb, pblock).max(axis=3) * np.log(2.0)) + _gamma(pblock)
                 s_lo = np.maximum(np.frexp(rb * (1 - dl))[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
                 s_hi = np.maximum(np.frexp(rb * (1 + dl))[1] - FP8_P_SUM_LOG2, -126).astype(np.float64)
-                ramb |= np.any((rb > 0) & (rb < 2.0 ** -100), axis=2)
+                # a block whose P̃ sum to less than 2^-100 may leave fp32's normal range in
+                # the kernel (its exp2 may flush them): bound its whole contribution instead
+                tiny = (rb > 0) & (rb < 2.0 ** -100)
                 ok = slot < nk
                 sv = vs[b, h][j]
                 vsl = np.zeros((tile, d))
@@ -490,6 +491,9 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                     xc2, r22, E22, sk2, rsc2 = second(sig2)
                     part2 = ambiguous_part(xc2, E22, sk2, rsc2) if round_p else 0.0
                     part = np.maximum(part, part2) + (np.abs(r22 - r2).sum(1) * sv)
+                if tiny.any():
+                    xt = np.where(np.repeat(tiny, pblock, axis=2)[..., :nk], x, 0.0)
+                    part = part + 2.125 * (xt.reshape(GR, nk) @ vabs)
                 if np.any(part):
                     amb += np.broadcast_to(part, (GR, d)).reshape(G, group, d)
             o = acc / ell[:, :, None]
@@ -500,7 +504,7 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
             out["lse"][b, h] = (m * np.log(2.0) + np.log(ell))[sel]
             out["ex_max"][b, h] = exm[sel]
             out["moves"][b, h] = mov[sel]
-            out["sched_amb"][b, h] = (np.broadcast_to(samb[:, None], (G, group)) | ramb)[sel]
+            out["sched_amb"][b, h] = np.broadcast_to(samb[:, None], (G, group))[sel]
     out["rows"] = allrows[live]
     out["n_tiles"] = n_tiles
     return out

@@ -116,6 +116,16 @@ def test_fwd_fp8_against_oracle(N, causal):
     _fwd_case(w)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_reference_max_moves(causal):
+    """Keys ×64: logits hundreds of octaves apart, so the reference max moves
+    past its 2^48 threshold several times a row and the 32-key blocks of P̃ take
+    scales far apart."""
+    w = W[2].with_(B=1, H=2, N=600, causal=causal, boost_frac=0.03, boost=64.0, wid=777 + causal)
+    _say("[case] fp8 forward, large logits", causal)
+    _fwd_case(w)
+
+
 def test_fwd_fp8_full_size_sampled():
     """The prefill workload (B1 H32 N4096 d128 causal, 1 % of key rows ×8):
     three heads, the 32-row groups of sampled rows (block edges, the last

@@ -376,7 +376,7 @@ def _instr_f32(a, b, acc, run_scale=None):
     return acc
 
 
-def _sim_fp32_kernel(q, k, v, scale, causal, rows):
+def _sim_fp32_kernel(q, k, v, scale, causal, rows, flush=False):
     """A float32 re-enactment of the FP8 forward's arithmetic, written apart from
     the model: logits from two float32 matrix instructions on the E4M3 codes times
     the block scales, exp2 and sums in float32, the reference max of each 32-row
@@ -384,8 +384,9 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows):
     row's 32-key half tile divided by 2^σ (σ from the float32 sum of the half)
     and rounded to E4M3 by torch's float8_e4m3fn conversion, the second product
     by the instruction on the keys in the V tile order with each run scaled by
-    its half's 2^σ, O = acc·(1/ℓ) rounded to bf16, L = m·scale + ln ℓ.  Returns
-    (O, L) on the rows of every 32-row group that holds one of ``rows``."""
+    its half's 2^σ, O = acc·(1/ℓ) rounded to bf16, L = m·scale + ln ℓ.  ``flush``:
+    exp2 returns 0 for results below fp32's normal range.  Returns (O, L) on the
+    rows of every 32-row group that holds one of ``rows``."""
     from oracle.fp8 import quantize_blocks
     (q8, qs), (k8, ks), (v8, vs) = (quantize_blocks(t, 64) for t in (q, k, v))
     B, H, N, d = q8.shape
@@ -432,6 +433,8 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows):
                     with np.errstate(invalid="ignore"):
                         x = np.exp2(s * c - (m * c)[:, None]).astype(np.float32)
                     x = np.where(np.isfinite(s), x, np.float32(0))
+                    if flush:
+                        x = np.where(x < np.float32(2.0 ** -126), np.float32(0), x)
                     half_sum = np.stack([x[:, :32].sum(axis=1, dtype=np.float32),
                                          x[:, 32:].sum(axis=1, dtype=np.float32)], axis=1)
                     sig = np.maximum(np.frexp(half_sum)[1] - 8, -126)
@@ -478,6 +481,23 @@ def test_fp32_kernel_simulation_passes(shape):
     rep = check_fp8(o, l, con)
     assert rep["pass"], rep
     assert rep["sched_amb_rows"] == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_kernel_simulation_with_large_logits(causal):
+    """Keys ×64: the logits span hundreds of octaves, the reference max moves
+    several times a row and many 32-key blocks sum to far below 2^-100 of it.
+    The fp32 re-enactment passes the tight rule whether its exp2 keeps
+    subnormal results or flushes them, and no row is left to the loose bound."""
+    w = synth.WORKLOADS[2].with_(B=1, H=2, N=600, causal=causal, boost_frac=0.03, boost=64.0, wid=777 + causal)
+    q, k, v = synth.make_prefill(w)
+    con = fp8_contract(q, k, v, w.scale, causal)
+    assert con["moves"].max() >= 4
+    for flush in (False, True):
+        o, l = _sim_fp32_kernel(q, k, v, w.scale, causal, con["rows"], flush=flush)
+        rep = check_fp8(o, l, con)
+        assert rep["pass"], (flush, rep)
+        assert rep["sched_amb_rows"] == 0
 
 
 def _slips(q, k, v, w, con):
