@@ -78,7 +78,7 @@ TRAFFIC_KERNELS = {
     "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "decode": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
     "gqa": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
-    "bwd": (["fa_bwd_prep_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"],
+    "bwd": (["fa_bwd_prep_kernel", "fa_bwd_dkdv_pair_kernel", "fa_bwd_dq_kernel"],
             ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]),
     "sparse": (["fa_fwd_kernel<128, false, true>"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "copy": (["copyBuffer"], []),

@@ -15,7 +15,9 @@
 //   fa_bwd_prep   per row: (L·log2 e, D) into the workspace;
 //   fa_bwd_dkdv   key/value blocks outside, query tiles inside — the loop
 //                 order of [15-779 L5] §7.4: a workgroup keeps dK and dV of
-//                 its 128 keys in registers and writes them once;
+//                 its 128 keys in registers and writes them once (by default
+//                 fa_bwd_dkdv_pair, eight wavefronts in pairs; the atomic and
+//                 block-sparse forms use fa_bwd_dkdv, four wavefronts);
 //   fa_bwd_dq     query blocks outside, key/value tiles inside, as in the
 //                 forward: dQ of 256 query rows stays in registers.
 // By default dQ is not accumulated with atomic adds from the key-block kernel
@@ -30,12 +32,14 @@
 // form takes about twice as long as the two-pass form.
 //
 // Layout on chip (64-lane wavefronts, v_mfma_f32_32x32x16_bf16):
-// * dkdv: each wavefront owns 32 keys.  The products are taken so that a
-//   lane's accumulator column is one key: S = Q Kᵀ and dP = dO Vᵀ with the
-//   key rows of K and V held in registers as the B operands; P and dS then
-//   sit in the layout of the B operand of dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS,
-//   whose A operands are read from the Q and dO tiles in LDS with the
-//   transpose load ds_read_b64_tr_b16.
+// * dkdv (four-wavefront form): each wavefront owns 32 keys.  The products
+//   are taken so that a lane's accumulator column is one key: S = Q Kᵀ and
+//   dP = dO Vᵀ with the key rows of K and V held in registers as the B
+//   operands; P and dS then sit in the layout of the B operand of
+//   dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, whose A operands are read from the Q and
+//   dO tiles in LDS with the transpose load ds_read_b64_tr_b16.
+// * dkdv_pair: the same products split over two wavefronts per 32 keys
+//   (layout at the kernel).
 // * dq: each wavefront owns 32 query rows, lane = query column as in the
 //   forward: Sᵀ = K Qᵀ and dPᵀ = V dOᵀ with Q and dO rows in registers, so
 //   L and D are one scalar per lane; dSᵀ feeds dQᵀ += Kᵀ dSᵀ directly, Kᵀ
@@ -646,6 +650,302 @@ __global__ __launch_bounds__(kBwdKvThreads, 1) void fa_bwd_dkdv_kernel(BwdParams
   }
 }
 
+// ---- dK, dV by wavefront pairs: key blocks outside, query tiles inside ------------
+// The same loop order as fa_bwd_dkdv_kernel ([15-779 L5] §7.4), with eight
+// wavefronts, two per SIMD, so that one wavefront's waits are covered by the
+// other's work.  The workgroup's 128 keys go to four pairs of 32; a pair's
+// products are split so that each wavefront fits the 256 registers a lane
+// has when two wavefronts share a SIMD:
+// * the score wavefront (0-3) holds the pair's K and V rows and, per step of
+//   64 queries, takes Sᵀ = K Qᵀ and dPᵀ = V dOᵀ with the query as the
+//   accumulator column (Q and dO rows read from LDS; L and D are then one
+//   pair of scalars per lane, loaded straight into registers), forms
+//   P = exp(scale·S − L) and dS = P ∘ (dP − D) in fp32 and writes both as
+//   bf16 to an LDS tile [query][key];
+// * the gradient wavefront (4-7) holds dK and dV of the pair's keys and, one
+//   step behind, adds dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, every operand read with
+//   the transpose load: dOᵀ and Qᵀ from the stage tiles, P and dS from the
+//   pair's tiles.  Their 8-byte chunks are XOR-swizzled by (query row / 2)
+//   mod 8: an 8-byte LDS write goes through in four passes of 16 consecutive
+//   lanes over 32 four-byte banks (measured with the conflict counter), and
+//   the score wavefront's 16 lanes of a pass write 16 rows, two per swizzle
+//   value; the transpose reads stay conflict-free too.
+// One barrier per step t: the score wavefronts take query tile t, the
+// gradient wavefronts tile t − 1 and issue the direct loads of tile t + 1 into
+// the buffers tile t − 2 has left (three stages of Q and dO, two of P and dS:
+// 160 KiB of LDS at d = 128).  P and dS are rounded at the same point, from
+// the same fp32 values, as in fa_bwd_dkdv_kernel.
+constexpr int kBwdPairThreads = 512;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdPairThreads, 1) void fa_bwd_dkdv_pair_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int BM = 64;            // query rows per step
+  constexpr int QT = BM * T::ROW;   // bytes of one Q (or dO) stage
+  constexpr int R = BM / T::RPR;    // direct loads per tensor per stage
+  constexpr int NG = 4;             // gradient wavefronts; they issue the stage loads
+  static_assert(R % NG == 0 && (NG * T::RPR) % 16 == 0, "stage loads spread evenly, one lane offset");
+  constexpr int PER = 2 * R / NG;   // stage loads per gradient wavefront
+  constexpr int XT = BM * 64;       // one P (or dS) tile: 64 queries × 32 keys, bf16
+  static_assert(kBwdBlockK == 4 * 32, "four pairs of 32 keys");
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds0[QT], q_lds1[QT], q_lds2[QT];
+  __shared__ __attribute__((aligned(16))) unsigned char o_lds0[QT], o_lds1[QT], o_lds2[QT];
+  __shared__ __attribute__((aligned(16))) unsigned char x_lds[2 * 4 * 2 * XT];  // [step parity][pair][P, dS]
+  unsigned char* const qbufs[3] = {q_lds0, q_lds1, q_lds2};
+  unsigned char* const obufs[3] = {o_lds0, o_lds1, o_lds2};
+
+  int bh, kb;
+  decode_kblock(p, bh, kb);
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave_u & 3;
+  const int i32 = lane & 31, g = lane >> 5, jj = lane & 15;
+  const int k0 = kb * kBwdBlockK;
+  const int kw = k0 + 32 * pair;  // first key of the pair
+  const size_t base = (size_t)bh * N * D;
+  const int first = CAUSAL ? k0 / BM : 0;  // query tiles before the block's first key see none of it
+  const int n_steps = ceil_div(N, BM) - first;
+  auto step_row = [&](int s) __attribute__((always_inline)) { return (first + s) * BM; };
+  // causal: the block's first two steps hold the diagonal; a pair whose keys
+  // all follow every query of a step skips it (both wavefronts alike)
+  auto skipped = [&](int s) __attribute__((always_inline)) { return CAUSAL && step_row(s) + BM - 1 < kw; };
+  unsigned char* const xpair = x_lds + pair * 2 * XT;  // + parity · 8·XT: P, then dS
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+
+  if (wave_u < 4) {
+    // ---------------- score wavefront ----------------
+    const __amdgpu_buffer_rsrc_t lrsrc = make_rsrc(p.ld + (size_t)bh * N * 2, N * 8);
+    bf16x8_t kf[T::KS], vf[T::KS];  // A operands: the K and V rows of key kw + i32
+    {
+      const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(p.k + base, N * T::ROW);
+      const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.v + base, N * T::ROW);
+#pragma unroll
+      for (int kk = 0; kk < T::KS; ++kk) {
+        kf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(krsrc, (kw + i32) * T::ROW + (2 * kk + g) * 16));
+        vf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(vrsrc, (kw + i32) * T::ROW + (2 * kk + g) * 16));
+      }
+    }
+    // (L·log2 e, D) of the lane's query in each 32-row half of a step
+    float2 ldc[2], ldn[2];
+    auto load_ld = [&](int s, float2(&dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dst[u] = buffer_load8(lrsrc, (step_row(s) + 32 * u + i32) * 8);
+    };
+    load_ld(0, ldc);
+    int row[T::KS];  // 16-byte row reads of Q and dO: row i32 (+32 per half), chunk 2kk + g
+#pragma unroll
+    for (int kk = 0; kk < T::KS; ++kk) row[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::swz(i32)) << 4);
+    int xw[4];  // P/dS writes: query row i32 (+32 per half), keys 8t + 4g .. +3
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xw[t] = i32 * 64 + 8 * ((2 * t + g) ^ ((i32 >> 1) & 7));
+    const float c = p.scale_log2;
+    wait_vmcnt<0>();
+    block_barrier();  // stage 0 is in
+
+    auto score = [&](int s, auto buf, auto masked) __attribute__((always_inline)) {
+      constexpr int B = decltype(buf)::value;
+      constexpr bool MASKED = decltype(masked)::value;
+      if (MASKED && skipped(s)) return;
+      const unsigned char* qb = qbufs[B];
+      const unsigned char* ob = obufs[B];
+      unsigned char* const xp = xpair + (s & 1) * 8 * XT;
+      unsigned char* const xs = xp + XT;
+      const int qs0 = step_row(s);
+#pragma unroll
+      for (int kk = 0; kk < T::KS; ++kk) asm volatile("" : "+v"(row[kk]));
+      constexpr int NA = 2 * T::KS;  // MFMAs per 32-query half (S and dP, KS k-steps each)
+      constexpr int LA = 6;          // operand reads in flight
+      static_assert(16 % NA == 0 && LA <= NA, "phase shapes");
+      f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sacc[u] = dpacc[u] = f32x16_t{};
+      // operand j: half j / NA, k-step (j % NA) / 2, a Q row (even j) or a dO row (odd j)
+      auto op = [&](int j) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(((j & 1) ? ob : qb) + row[(j % NA) >> 1] +
+                                                                             (j / NA) * 32 * T::ROW));
+      };
+      auto mfma = [&](int j, bf16x8_t b) __attribute__((always_inline)) {
+        const int u = j / NA, kk = (j % NA) >> 1;
+        if (j & 1)
+          dpacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk], b, dpacc[u], 0, 0, 0);
+        else
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], b, sacc[u], 0, 0, 0);
+      };
+      // element r of half u: key kw + 8(r/4) + 4g + r%4, query qs0 + 32u + i32
+      float pe[4], se[4];
+      auto soft_el = [&](int u, int r) __attribute__((always_inline)) {
+        float e = __builtin_amdgcn_exp2f(fmaf(sacc[u][r], c, -ldc[u].x));
+        if (MASKED && kw + 8 * (r >> 2) + 4 * g + (r & 3) > qs0 + 32 * u + i32) e = 0.f;
+        pe[r & 3] = e;
+        se[r & 3] = e * (dpacc[u][r] - ldc[u].y);
+        if ((r & 3) == 3) {
+          const int o = u * 32 * 64 + xw[r >> 2];
+          *reinterpret_cast<u32x2_t*>(xp + o) = u32x2_t{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
+          *reinterpret_cast<u32x2_t*>(xs + o) = u32x2_t{pack_bf16x2(se[0], se[1]), pack_bf16x2(se[2], se[3])};
+        }
+      };
+      bf16x8_t ra[LA];
+#pragma unroll
+      for (int j = 0; j < LA; ++j) ra[j] = op(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {  // S, dP of half 0
+        mfma(j, ra[j % LA]);
+        ra[j % LA] = op(j + LA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = NA; j < 2 * NA; ++j) {  // S, dP of half 1 with P, dS of half 0
+        mfma(j, ra[j % LA]);
+        if (j + LA < 2 * NA) ra[j % LA] = op(j + LA);
+#pragma unroll
+        for (int r = (j - NA) * (16 / NA); r < (j - NA + 1) * (16 / NA); ++r) soft_el(0, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) soft_el(1, r);  // P, dS of half 1
+    };
+    auto phase = [&](int t, auto buf, auto masked) __attribute__((always_inline)) {
+      load_ld(t + 1, ldn);
+      if (t < n_steps) score(t, buf, masked);
+      wait_vmcnt<0>();
+      block_barrier();  // tile t + 1 is in; P and dS of tile t are complete
+#pragma unroll
+      for (int u = 0; u < 2; ++u) ldc[u] = ldn[u];
+    };
+    if (CAUSAL) {
+      phase(0, I0{}, std::true_type{});
+      phase(1, I1{}, std::true_type{});
+    } else {
+      phase(0, I0{}, std::false_type{});
+      phase(1, I1{}, std::false_type{});
+    }
+    for (int t = 2; t <= n_steps; t += 3) {
+      phase(t, I2{}, std::false_type{});
+      if (t + 1 <= n_steps) phase(t + 1, I0{}, std::false_type{});
+      if (t + 2 <= n_steps) phase(t + 2, I1{}, std::false_type{});
+    }
+    return;
+  }
+
+  // ---------------- gradient wavefront ----------------
+  const int gw = wave_u - 4;
+  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc(p.q + base, N * T::ROW);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(p.dout + base, N * T::ROW);
+  // Stage loads: gradient wavefront gw issues loads gw, gw + NG, ... of the 2R
+  // runs (Q runs first, then dO); the lane's offset is the same for all of
+  // them.  Stages past the last read zeros into a buffer nobody reads.
+  const int x0 = gw % R;
+  const int goff = run_goff<D>(x0, lane);
+  auto issue = [&](int s, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    const int toff = step_row(s) * T::ROW;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = gw + i * NG;
+      if (i * NG < R)
+        load_lds16(qrsrc, qbufs[B] + x * 1024, goff + toff + (x - x0) * 1024);
+      else
+        load_lds16(orsrc, obufs[B] + (x - R) * 1024, goff + toff + (x - R - x0) * 1024);
+    }
+  };
+  int tr0[T::DSUB], tr8[T::DSUB];  // transpose reads of the stage tiles
+#pragma unroll
+  for (int ds = 0; ds < T::DSUB; ++ds) {
+    tr0[ds] = TileReads<D>::tr_off(lane, ds, 0);
+    tr8[ds] = TileReads<D>::tr_off(lane, ds, 1);
+  }
+  // transpose reads of a P/dS tile, k-step kk: rows 16kk + 4g + jj/4 (+8),
+  // keys 16·((lane/16) mod 2) + 4·(jj mod 4) .. +3
+  int xr[2];
+#pragma unroll
+  for (int pl = 0; pl < 2; ++pl)
+    xr[pl] = (4 * g + (jj >> 2) + 8 * pl) * 64 + 8 * ((4 * ((lane >> 4) & 1) + (jj & 3)) ^ (2 * g + (jj >> 3) + 4 * pl));
+  f32x16_t dk[T::DSUB], dv[T::DSUB];
+#pragma unroll
+  for (int ds = 0; ds < T::DSUB; ++ds) dk[ds] = dv[ds] = f32x16_t{};
+  issue(0, I0{});
+  wait_vmcnt<0>();
+  block_barrier();  // stage 0 is in
+
+  auto grad = [&](int s, auto buf, auto masked) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    if (decltype(masked)::value && skipped(s)) return;
+    const unsigned char* qb = qbufs[B];
+    const unsigned char* ob = obufs[B];
+    const unsigned char* xp = xpair + (s & 1) * 8 * XT;
+    const unsigned char* xs = xp + XT;
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(tr0[ds]), "+v"(tr8[ds]));
+    constexpr int NC = 2 * T::DSUB;  // MFMAs per k-step (dV and dK of each 32-wide d sub-tile)
+    constexpr int NM = 4 * NC;       // MFMAs per step (four k-steps of 16 queries)
+    constexpr int LC = 4;            // operand reads in flight
+    auto xop = [&](const unsigned char* x, int kk) __attribute__((always_inline)) {
+      const u32x2_t a0 = lds_tr_read(x, xr[0] + kk * 16 * 64);
+      const u32x2_t a1 = lds_tr_read(x, xr[1] + kk * 16 * 64);
+      return __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+    };
+    // MFMA m: k-step m / NC, d sub-tile (m / 2) mod DSUB; dV (even m: dOᵀ, P) or dK (odd m: Qᵀ, dS)
+    auto op = [&](int m) __attribute__((always_inline)) {
+      return TileReads<D>::tr_at((m & 1) ? qb : ob, tr0[(m >> 1) % T::DSUB], tr8[(m >> 1) % T::DSUB], m / NC);
+    };
+    bf16x8_t pop[2], sop[2];  // B operands of the current and the next k-step
+    bf16x8_t ra[LC];
+    pop[0] = xop(xp, 0);
+    sop[0] = xop(xs, 0);
+#pragma unroll
+    for (int m = 0; m < LC; ++m) ra[m] = op(m);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int kk = m / NC, ds = (m >> 1) % T::DSUB;
+      if (m & 1)
+        dk[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % LC], sop[kk & 1], dk[ds], 0, 0, 0);
+      else
+        dv[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % LC], pop[kk & 1], dv[ds], 0, 0, 0);
+      if (m + LC < NM) ra[m % LC] = op(m + LC);
+      if (m % NC == 0 && kk + 1 < 4) {
+        pop[(kk + 1) & 1] = xop(xp, kk + 1);
+        sop[(kk + 1) & 1] = xop(xs, kk + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto phase = [&](int t, auto buf, auto masked) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;  // t mod 3: tile t − 1 is in buffer B + 2, tile t + 1 goes to B + 1
+    issue(t + 1, std::integral_constant<int, (B + 1) % 3>{});
+    if (t >= 1) grad(t - 1, std::integral_constant<int, (B + 2) % 3>{}, masked);
+    wait_vmcnt<0>();
+    block_barrier();
+  };
+  if (CAUSAL) {
+    phase(0, I0{}, std::true_type{});
+    phase(1, I1{}, std::true_type{});
+  } else {
+    phase(0, I0{}, std::false_type{});
+    phase(1, I1{}, std::false_type{});
+  }
+  for (int t = 2; t <= n_steps; t += 3) {
+    phase(t, I2{}, std::false_type{});
+    if (t + 1 <= n_steps) phase(t + 1, I0{}, std::false_type{});
+    if (t + 2 <= n_steps) phase(t + 2, I1{}, std::false_type{});
+  }
+
+  // ---- epilogue: dK = scale · Σ dSᵀ Q, dV = Σ Pᵀ dO, staged in the (now free)
+  // Q and dO stage buffers: region 2·gw for dK, 2·gw + 1 for dV
+  {
+    constexpr int RG = 32 * T::ROW;
+    static_assert(2 * RG == QT, "two staging regions per stage buffer");
+    unsigned char* const kst = gw == 0 ? q_lds0 : gw == 1 ? q_lds1 : gw == 2 ? q_lds2 : o_lds0;
+    const int valid = min(32, N - kw);
+    store_rows_staged<D>(dk, p.scale, kst, p.dk + base + (size_t)kw * D, valid, lane);
+    store_rows_staged<D>(dv, 1.f, kst + RG, p.dv + base + (size_t)kw * D, valid, lane);
+  }
+}
+
 // ---- dQ: query blocks outside, key/value tiles inside -----------------------------
 __device__ inline void decode_qblock(const BwdParams& p, int& bh, int& qb) {
   const int x = blockIdx.x;
@@ -940,8 +1240,9 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_dq_finish_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, false, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
-                     stream, p);
+  static const hipError_t pattr = allow_full_lds(&fa_bwd_dkdv_pair_kernel<D, CAUSAL>);
+  if (pattr != hipSuccess) return pattr;
+  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3(p.BH * p.n_kblk), dim3(kBwdPairThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
