@@ -36,7 +36,6 @@ namespace fa {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFp8RescaleLog2 = 48.0f;          // P̃ ≤ 2^48 against the reference max
 constexpr float kFp8SumBound = 281474976710656.0f;  // 2^48: a lane's sum at most this bounds its elements
@@ -163,13 +162,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kFwdThreads), amdgpu_wa
 void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int* __restrict__ vs_all) {
   using T = Fp8Tile;
   constexpr int SROW = 2 * kFp8D + 16;  // staging row stride of the bf16 output (bytes)
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES],
-      k_lds2[T::TILE_BYTES], k_lds3[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES],
-      v_lds2[T::TILE_BYTES], v_lds3[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char stg_all[kFwdWaves * 32 * SROW];
-  unsigned char* const kbufs[4] = {k_lds0, k_lds1, k_lds2, k_lds3};
-  unsigned char* const vbufs[4] = {v_lds0, v_lds1, v_lds2, v_lds3};
+  // One LDS array with the eight tile buffers first: every tile read then has
+  // an address below 64 KiB and takes it as the instruction's immediate offset
+  // (placed after the output staging, half of them needed an address add a read).
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[8 * T::TILE_BYTES + kFwdWaves * 32 * SROW];
+  unsigned char* const kbufs[4] = {lds_all, lds_all + T::TILE_BYTES, lds_all + 2 * T::TILE_BYTES, lds_all + 3 * T::TILE_BYTES};
+  unsigned char* const vbufs[4] = {lds_all + 4 * T::TILE_BYTES, lds_all + 5 * T::TILE_BYTES, lds_all + 6 * T::TILE_BYTES,
+                                   lds_all + 7 * T::TILE_BYTES};
+  unsigned char* const stg_all = lds_all + 8 * T::TILE_BYTES;
 
   int bh, qb;
   fp8_decode_work(p, bh, qb);
@@ -331,10 +331,14 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int w4 = 2 * (part & 1) + h;
-      s16x2_t x = {0, 0};
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, pe[sub][4 * w4], pe[sub][4 * w4 + 1], sc, false);
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, pe[sub][4 * w4 + 2], pe[sub][4 * w4 + 3], sc, true);
-      pb[4 * sub + w4] = __builtin_bit_cast(int, x);
+      // the two conversions fill the low and the high half of the word; the
+      // first is declared as writing the whole register, so that no value is
+      // prepared for the half it keeps (the second overwrites that half)
+      int w;
+      asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3" : "=v"(w) : "v"(pe[sub][4 * w4]), "v"(pe[sub][4 * w4 + 1]), "v"(sc));
+      asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]"
+          : "+v"(w) : "v"(pe[sub][4 * w4 + 2]), "v"(pe[sub][4 * w4 + 3]), "v"(sc));
+      pb[4 * sub + w4] = w;
     }
     if (part == 3) psc = kE8M0One + (g ? sig[1] : sig[0]);
   };
