@@ -78,7 +78,7 @@ TRAFFIC_KERNELS = {
     "fwd": (["fa_fwd_kernel"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "decode": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
     "gqa": (["fa_decode_split_kernel", "fa_decode_combine_kernel"], ["fa_decode.hip", "fa_internal.h"]),
-    "bwd": (["fa_bwd_prep_kernel", "fa_bwd_dkdv_pair_kernel", "fa_bwd_dq_kernel"],
+    "bwd": (["fa_bwd_dq_kernel", "fa_bwd_dkdv_pair_kernel"],
             ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]),
     "sparse": (["fa_fwd_kernel<128, false, true>"], ["fa_fwd.hip", "fa_device.h", "fa_internal.h"]),
     "copy": (["copyBuffer"], []),
@@ -503,8 +503,8 @@ def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
            "algorithmic_flops": flops,
            "algorithmic_bytes": float(wf.B * wf.H * (16 * wf.N * wf.d + 4 * wf.N)),
            "traffic": traffic_bytes(traffic, "bwd"),
-           "note": "three kernels per call (per-row L and D; dK, dV; dQ); the dQ pass recomputes S and dP, "
-                   "so the matrix cores run 7/5 of the counted FLOPs"}
+           "note": "two kernels per call (dQ, which also forms the per-row L and D; then dK, dV); the dQ pass "
+                   "recomputes S and dP, so the matrix cores run 7/5 of the counted FLOPs"}
     if args.no_bwd_atomic:
         return res
     # the one-pass form with atomic dQ, timed the same way for comparison

@@ -11,7 +11,7 @@
 //     dV = Σ Pᵀ dO,   dK = scale · Σ dSᵀ Q,   dQ = scale · Σ dS K.
 // ([15-779 L5] §7.1; [pinghaoyang FA-1] "Backward".)
 //
-// Three kernels, in stream order:
+// The kernels:
 //   fa_bwd_prep   per row: (L·log2 e, D) into the workspace;
 //   fa_bwd_dkdv   key/value blocks outside, query tiles inside — the loop
 //                 order of [15-779 L5] §7.4: a workgroup keeps dK and dV of
@@ -20,6 +20,10 @@
 //                 block-sparse forms use fa_bwd_dkdv, four wavefronts);
 //   fa_bwd_dq     query blocks outside, key/value tiles inside, as in the
 //                 forward: dQ of 256 query rows stays in registers.
+// Stream order: by default fa_bwd_dq (which forms the per-row pairs itself,
+// as fa_bwd_prep would, and writes them) then fa_bwd_dkdv_pair; the
+// block-sparse form runs prep, dkdv, dq; the atomic form prep, dkdv<FUSED>,
+// then fa_bwd_dq_finish.
 // By default dQ is not accumulated with atomic adds from the key-block kernel
 // (the scheme of [15-779 L5] §7.4); its own pass recomputes S and dP instead,
 // which costs two more tile products (seven in all, against five) but keeps
@@ -1001,7 +1005,37 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
       qf[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(qrsrc, q_row * T::ROW + (2 * kk + g) * 16));
       of[kk] = __builtin_bit_cast(bf16x8_t, buffer_load16(orsrc, q_row * T::ROW + (2 * kk + g) * 16));
     }
-    ld = buffer_load8(make_rsrc(p.ld + (size_t)bh * N * 2, N * 8), q_row * 8);
+    if constexpr (SPARSE) {
+      ld = buffer_load8(make_rsrc(p.ld + (size_t)bh * N * 2, N * 8), q_row * 8);
+    } else {
+      // (L·log2 e, D = dO·O) of this lane's row formed here and written to the
+      // workspace for the dK/dV kernel, which runs after this one.  The per-row
+      // kernel's arithmetic in its order — each 16-byte chunk's eight products
+      // in turn, then the chunks pairwise at index distance 8, 4, 2, 1 (the lane
+      // holds the even or the odd chunks) — so D is the same bit for bit as in
+      // the backward forms that keep that kernel.
+      const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(p.o + base, N * T::ROW);
+      float part[T::KS];
+#pragma unroll
+      for (int kk = 0; kk < T::KS; ++kk) {
+        const u32x4_t o = buffer_load16(o_rsrc, q_row * T::ROW + (2 * kk + g) * 16);
+        const u32x4_t d = __builtin_bit_cast(u32x4_t, of[kk]);
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(d[e] << 16), a);
+          a = fmaf(__uint_as_float(o[e] & 0xffff0000u), __uint_as_float(d[e] & 0xffff0000u), a);
+        }
+        part[kk] = a;
+      }
+#pragma unroll
+      for (int w = T::KS / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) part[i] = part[i] + part[i + w];
+      const float lse = q_row < N ? p.lse[(size_t)bh * N + q_row] : 0.f;
+      ld = make_float2(lse * 1.4426950408889634f, pair_sum(part[0]));
+      if (g == 0 && q_row < N) reinterpret_cast<float2*>(p.ld)[(size_t)bh * N + q_row] = ld;
+    }
   }
 
   TileReads<D> rd;
@@ -1215,8 +1249,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  const int rows_per_block = 256 / (D / 8);
   const long long rows = (long long)p.BH * p.N;
+  if (!p.block_mask && !p.dqacc) {
+    // the default form: the dQ kernel forms the per-row (L, D) itself and
+    // writes them for the dK/dV kernel, which therefore runs second
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    static const hipError_t pattr = allow_full_lds(&fa_bwd_dkdv_pair_kernel<D, CAUSAL>);
+    if (pattr != hipSuccess) return pattr;
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3(p.BH * p.n_kblk), dim3(kBwdPairThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
+  const int rows_per_block = 256 / (D / 8);
   hipLaunchKernelGGL((fa_bwd_prep_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
                      0, stream, p);
   hipError_t e = hipGetLastError();
@@ -1229,23 +1275,14 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, true>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
     return hipGetLastError();
   }
-  if (p.dqacc) {
-    static const hipError_t attr = allow_full_lds(&fa_bwd_dkdv_kernel<D, CAUSAL, true, false>);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, true, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
-                       stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long n8 = rows * D / 8;
-    hipLaunchKernelGGL((fa_bwd_dq_finish_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
-  static const hipError_t pattr = allow_full_lds(&fa_bwd_dkdv_pair_kernel<D, CAUSAL>);
-  if (pattr != hipSuccess) return pattr;
-  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3(p.BH * p.n_kblk), dim3(kBwdPairThreads), 0, stream, p);
+  static const hipError_t attr = allow_full_lds(&fa_bwd_dkdv_kernel<D, CAUSAL, true, false>);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, true, false>), dim3(p.BH * p.n_kblk), dim3(kBwdKvThreads), 0,
+                     stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, false>), dim3(p.BH * p.n_qblk), dim3(kFwdThreads), 0, stream, p);
+  const long long n8 = rows * D / 8;
+  hipLaunchKernelGGL((fa_bwd_dq_finish_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
