@@ -128,9 +128,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  *   workspace : device buffer of at least fa_bwd_workspace_bytes(B, H, N)
  *             bytes, 16-byte aligned, owned by the caller; contents on entry
  *             ignored, on exit unspecified; calls sharing it must be ordered.
- * Three kernels run in stream order: the per-row (L, D) pass, then dK and dV
- * (key blocks outside, query tiles inside, [15-779 L5] §7.4), then dQ (query
- * blocks outside).  Errors as for fa_fwd; FA_ERR_WORKSPACE for a missing or
+ * Two kernels run in stream order: dQ (query blocks outside), which also forms
+ * each row's (L, D) pair into the workspace, then dK and dV (key blocks
+ * outside, query tiles inside, [15-779 L5] §7.4), which read the pairs.
+ * Errors as for fa_fwd; FA_ERR_WORKSPACE for a missing or
  * short workspace; FA_ERR_ALIAS when an output or the workspace overlaps an
  * input or another output.  B·H·N must stay below 2^31. */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
