@@ -70,8 +70,6 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdStages = 3;  // LDS stages per tensor (loops are unrolled by this)
-
 template <int D>
 struct BwdTile {
   static constexpr int CH = D / 8;        // 16-byte chunks per row
@@ -145,15 +143,6 @@ __device__ inline int run_goff(int x0, int lane) {
   using T = BwdTile<D>;
   const int r = x0 * T::RPR + lane / T::CH;
   return r * T::ROW + (((lane % T::CH) ^ T::swz(r)) << 4);
-}
-
-// Packs 8 fp32 accumulator elements r0 .. r0+7 as the bf16 B operand of a
-// product reducing over the accumulator's rows (row order as in the forward).
-__device__ inline bf16x8_t pack8(const float* x) {
-  u32x4_t w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // Writes a wavefront's 32 output rows, held as fp32 accumulators whose lane is
