@@ -157,7 +157,6 @@ def cpu_baseline(wf, wd, q, k, v, qd, kd, vd, budget_s):
     threads = min(len(os.sched_getaffinity(0)), 16)
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ.setdefault(var, str(threads))
-    import numpy as np
     from oracle import attention_ref, decode_ref
     try:
         from threadpoolctl import threadpool_info, threadpool_limits

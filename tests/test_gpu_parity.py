@@ -5,7 +5,6 @@ Rule (oracle/compare.py): |O − O_ref| ≤ 1e-2 + ½·ulp_bf16(O_ref) per eleme
 and |LSE − LSE_ref| ≤ 1e-3, with the literal max-abs error reported beside.
 """
 
-import math
 import sys
 
 import numpy as np
@@ -16,7 +15,6 @@ torch = pytest.importorskip("torch")
 import exact_attention_31_amd as fa
 import synth
 from oracle import attention_ref, decode_gqa_ref, decode_ref, check_prefill
-from oracle.compare import bf16_half_ulp
 
 pytestmark = pytest.mark.gpu
 

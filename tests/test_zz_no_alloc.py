@@ -4,7 +4,6 @@ outputs equal fa_decode's bit for bit, and fa_decode matches the oracle."""
 
 import sys
 
-import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
