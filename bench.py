@@ -6,7 +6,9 @@ One step = one pass of the whole path over resident synthetic inputs:
   * decode   fa_decode B16 H32 Lkv32768 d128, 64 KV splits, bf16
 W untimed warm-up steps, then K timed steps between device synchronisations.
 Each call is also timed with HIP events recorded on the stream it runs on
-(torch's current stream), which gives the per-kernel figures:
+(torch's current stream), created with hipEventDisableSystemFence so that
+recording them adds no cache writeback or invalidation between the calls;
+they give the per-kernel figures:
   * value            prefill TFLOP/s = 4·N²·d·B·H / 2 (causal) ÷ fa_fwd time
   * decode.value     GB/s of algorithmic bytes (K, V once; q in; O, LSE out)
   * roofline         fa_fwd against the bf16 dense MFMA peak (2.5166 PFLOP/s)
@@ -64,12 +66,78 @@ def parse():
     ap.add_argument("--no-bwd-atomic", action="store_true",
                     help="skip the fa_bwd_atomic comparison in the backward leg (counter runs of fa_bwd alone)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
+    ap.add_argument("--events", choices=["nofence", "torch"], default="nofence",
+                    help="timing events: HIP events created with hipEventDisableSystemFence (default; recording "
+                         "one writes back and invalidates no cache), or torch.cuda.Event (a system-scope fence "
+                         "at each record)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 --pmc (JSON), if present")
     ap.add_argument("--make-traffic", metavar="DIR",
                     help="write --traffic from rocprofv3 --pmc csv output under DIR/<COUNTER>_<kind>/ "
                          "(COUNTER in FETCH_SIZE, WRITE_SIZE; kind in fwd, decode, gqa, bwd, sparse, copy) and exit")
     return ap.parse_args()
+
+
+class HipTimingEvent:
+    """A HIP event used only to time work on torch's current stream, created with
+    hipEventDisableSystemFence: recording it performs no system-scope fence, so it
+    neither writes back and invalidates the caches nor delays the next kernel (which
+    a default event does at every record).  Same interface as torch.cuda.Event."""
+    _hip = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:  # the HIP runtime torch (and libfa.so) already use
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            hip = ctypes.CDLL(path or "libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self._torch, self._ctypes = torch, ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self.runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)  # hipEventDisableSystemFence
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = self.runtime().hipEventRecord(self.ev, self._ctypes.c_void_p(self._torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        ms = self._ctypes.c_float()
+        rc = self.runtime().hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self.ev and HipTimingEvent._hip is not None:
+            HipTimingEvent._hip.hipEventDestroy(self.ev)
+
+
+EVENT_KIND = "nofence"
+
+
+def Event():
+    """A timing event of the kind --events selects."""
+    if EVENT_KIND == "torch":
+        import torch
+        return torch.cuda.Event(enable_timing=True)
+    return HipTimingEvent()
 
 
 # Kernels whose HBM bytes are reported, and the sources each one is built from: a traffic
@@ -200,7 +268,7 @@ def copy_reference(torch, dev, args):
     for _ in range(args.warmup):
         dst.copy_(src)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = Event(), Event()
     a.record()
     for _ in range(args.steps):
         dst.copy_(src)
@@ -223,7 +291,7 @@ def time_gqa(torch, fa, synth, dev, args, traffic):
     for _ in range(args.warmup):
         fa.fa_decode_gqa(qg, kg, vg, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[Event() for _ in range(2)] for _ in range(args.steps)]
     for e in evs:
         e[0].record()
         fa.fa_decode_gqa(qg, kg, vg, scale=wg.scale, num_splits=wg.num_splits, workspace=ws)
@@ -328,7 +396,7 @@ def time_prefill_workloads(torch, fa, synth, dev, args):
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        ev = [[Event() for _ in range(2)] for _ in range(args.steps)]
         for e in ev:
             e[0].record()
             call()
@@ -350,7 +418,7 @@ def time_prefill_workloads(torch, fa, synth, dev, args):
                 call()
         graph.replay()
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0, g1 = Event(), Event()
         g0.record()
         graph.replay()
         g1.record()
@@ -395,7 +463,7 @@ def time_fp8(torch, fa, synth, dev, args):
             fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
             fa.fa_quantize_fp8(q, k, v, packed=packed)
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        ev = [[Event() for _ in range(6)] for _ in range(args.steps)]
         for e in ev:
             e[0].record()
             fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale, causal=w.causal, out=o, lse=lse)
@@ -430,7 +498,7 @@ def time_sparse(torch, fa, synth, dev, args, traffic):
         fa.fa_fwd_block_sparse(q, k, v, md, scale=ws_.scale, out=o, lse=lse)
         fa.fa_fwd(q, k, v, scale=ws_.scale, out=o, lse=lse)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[Event() for _ in range(4)] for _ in range(args.steps)]
     for e in ev:
         e[0].record()
         fa.fa_fwd_block_sparse(q, k, v, md, scale=ws_.scale, out=o, lse=lse)
@@ -487,7 +555,7 @@ def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
     for _ in range(args.warmup):
         fa.fa_bwd(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=ws)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[Event() for _ in range(2)] for _ in range(args.steps)]
     for e in evs:
         e[0].record()
         fa.fa_bwd(q, k, v, o, lse, do, scale=wf.scale, causal=wf.causal, workspace=ws)
@@ -525,6 +593,8 @@ def time_bwd(torch, fa, synth, dev, args, wf, q, k, v, traffic):
 
 def main():
     args = parse()
+    global EVENT_KIND
+    EVENT_KIND = args.events
     if args.make_traffic:
         return make_traffic(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -585,7 +655,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[Event() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -630,6 +700,8 @@ def main():
         },
     }
     out["device"] = device_facts(torch)
+    out["timing"] = ("HIP events on the launch stream, created with hipEventDisableSystemFence" if args.events == "nofence"
+                     else "torch.cuda.Event on the launch stream (system-scope fence at each record)")
     if f_avg:
         tf = flops / (f_avg * 1e-3) / 1e12
         out["prefill"] = {"ms": round(f_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tf, 2),
