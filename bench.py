@@ -106,27 +106,31 @@ class HipTimingEvent:
     def __init__(self):
         import ctypes
         import torch
-        self._torch, self._ctypes = torch, ctypes
+        self._torch, self._ctypes, self._hip = torch, ctypes, self.runtime()
         self.ev = ctypes.c_void_p()
-        rc = self.runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)  # hipEventDisableSystemFence
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)  # hipEventDisableSystemFence
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
 
     def record(self):
-        rc = self.runtime().hipEventRecord(self.ev, self._ctypes.c_void_p(self._torch.cuda.current_stream().cuda_stream))
+        rc = self._hip.hipEventRecord(self.ev, self._ctypes.c_void_p(self._torch.cuda.current_stream().cuda_stream))
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_time(self, end):
         ms = self._ctypes.c_float()
-        rc = self.runtime().hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev)
+        rc = self._hip.hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev)
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
     def __del__(self):
-        if self.ev and HipTimingEvent._hip is not None:
-            HipTimingEvent._hip.hipEventDestroy(self.ev)
+        hip = getattr(self, "_hip", None)
+        if hip is not None and self.ev:
+            try:
+                hip.hipEventDestroy(self.ev)
+            except Exception:  # interpreter shutdown
+                pass
 
 
 EVENT_KIND = "nofence"
