@@ -104,8 +104,10 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   p.lse = lse;
   p.BH = B * H;
   p.N = N;
-  p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
+  // block-sparse: one workgroup per query block of the mask (kSparseBlock rows)
+  p.n_qblk = block_mask ? nb : fa::ceil_div(N, fa::kFwdBlockM);
   const long long total = (long long)p.BH * p.n_qblk;
+  if (total > 0x7fffffffll) return FA_ERR_SHAPE;
   p.xcd_remap = (total % 8 == 0) && ((total / 8) % p.n_qblk == 0);
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;

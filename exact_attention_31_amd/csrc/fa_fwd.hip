@@ -125,9 +125,13 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
 
 // SPARSE: block-sparse attention ([FA-1拆解] "块稀疏扩展"): a mask over blocks
 // of kSparseBlock query rows × kSparseBlock keys switches whole score blocks
-// off.  The workgroup lists the key blocks either of its two query blocks
-// keeps and streams only those; a wavefront treats a listed key tile its own
-// query block does not keep like a tile above the diagonal (never visited).
+// off.  A workgroup owns one query block of kSparseBlock rows and streams only
+// the key blocks its mask row keeps.  Wavefronts w and w + 4 own the same 32
+// rows and take the two 32-key halves of every tile (group 0 the first, group
+// 1 the second), so both groups work on every streamed tile; each keeps its own
+// running (m, ℓ, accumulator) over its halves, and group 1 hands its summary to
+// group 0 through LDS at the end, where the two are merged with ⊕ ([15-779 L5]
+// §4.4) before the one division.
 //
 // Causal d = 64 runs two workgroups per CU (64 KiB of LDS each, registers held
 // to 128 a lane): a CU then overlaps one block's prologue and epilogue with
@@ -139,15 +143,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kFwdThreads),
                           amdgpu_waves_per_eu(D == 64 && CAUSAL ? 4 : 2)))
 void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
-  static_assert(kSparseBlock == 2 * T::BN && kFwdBlockM == 2 * kSparseBlock, "two tiles per key block, two query blocks per workgroup");
+  static_assert(kSparseBlock == 2 * T::BN && kSparseBlock == 32 * (kFwdWaves / 2),
+                "two tiles per key block; SPARSE: four wavefronts of 32 rows per query block");
+  // per wavefront and tile: 32-key sub-tiles of Sᵀ and 16-key k-steps of Oᵀ += Vᵀ P̃ᵀ
+  // (SPARSE: one 32-key half of each tile per wavefront group)
+  constexpr int NSUB_W = SPARSE ? 1 : T::NSUB;
+  constexpr int KSPV_W = SPARSE ? T::KS_PV / 2 : T::KS_PV;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[T::TILE_BYTES], k_lds1[T::TILE_BYTES],
       k_lds2[T::TILE_BYTES], k_lds3[T::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[T::TILE_BYTES], v_lds1[T::TILE_BYTES],
       v_lds2[T::TILE_BYTES], v_lds3[T::TILE_BYTES];
   unsigned char* const kbufs[4] = {k_lds0, k_lds1, k_lds2, k_lds3};
   unsigned char* const vbufs[4] = {v_lds0, v_lds1, v_lds2, v_lds3};
-  // SPARSE: the kept key blocks, bits 0-13 the block, bit 14 (15) set when the
-  // first (second) query block of the workgroup keeps it
+  // SPARSE: the key blocks the workgroup's query block keeps, in order
   __shared__ uint16_t kblocks[SPARSE ? kSparseMaxBlocks : 1];
 
   int bh, qb;
@@ -160,11 +168,12 @@ void fa_fwd_kernel(FwdParams p) {
   const int g = lane >> 5;    // which 32-lane half
   const int jj = lane & 15;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
-  const int q0 = qb * kFwdBlockM;
-  const int wq0 = q0 + wave_u * 32;  // first query row of this wavefront (uniform)
-  const int q_row = wq0 + i32;
-  const size_t base = (size_t)bh * N * D;
   const int grp = wave_u >> 2;  // wavefronts w and w+4 share a SIMD and alternate phases
+  const int q0 = qb * (SPARSE ? kSparseBlock : kFwdBlockM);
+  const int wq0 = q0 + (SPARSE ? wave_u & 3 : wave_u) * 32;  // first query row of this wavefront (uniform)
+  const int q_row = wq0 + i32;
+  const int kh = SPARSE ? 32 * grp : 0;  // first key of this wavefront's part of a tile
+  const size_t base = (size_t)bh * N * D;
 
   // Direct global->LDS loads, a tile issued by the four wavefronts of a group
   // (K by group 0, V by group 1): wavefront w (w & 3 = u), load i fills LDS
@@ -184,14 +193,14 @@ void fa_fwd_kernel(FwdParams p) {
   // Operand-read lane offsets (bytes within a tile).
   int k_rd[T::KS_QK];  // K rows i32 (+32 per sub-tile), chunk 2kk + g
 #pragma unroll
-  for (int kk = 0; kk < T::KS_QK; ++kk) k_rd[kk] = i32 * T::ROW + (((2 * kk + g) ^ T::k_swz(i32)) << 4);
+  for (int kk = 0; kk < T::KS_QK; ++kk) k_rd[kk] = (kh + i32) * T::ROW + (((2 * kk + g) ^ T::k_swz(i32)) << 4);
   int v_rd[T::DSUB];   // transpose reads: rows 4g + jj/4 (+16kk, +8), dims 32ds + 16(G&1) + 4(jj&3)
   {
     const int r = 4 * g + (jj >> 2);
     const int cl = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds)
-      v_rd[ds] = r * T::ROW + (((4 * ds + cl) ^ T::v_swz(r)) << 4) + 8 * (jj & 1);
+      v_rd[ds] = (kh + r) * T::ROW + (((4 * ds + cl) ^ T::v_swz(r)) << 4) + 8 * (jj & 1);
   }
 
   // Q fragments: the B operand of Sᵀ = K Qᵀ (lane: query q_row, dims 16kk + 8g .. +7).
@@ -207,21 +216,18 @@ void fa_fwd_kernel(FwdParams p) {
 
   int n_tiles;
   if constexpr (SPARSE) {
-    // wavefront 0 compacts the kept key blocks of the two query blocks into
-    // kblocks (ballot + running count); causal: none past the block's last row
-    const int rb0 = q0 / kSparseBlock;
-    const bool two = rb0 + 1 < p.mask_tq;
-    const uint8_t* m0 = p.block_mask + ((size_t)(p.mask_heads == 1 ? 0 : bh) * p.mask_tq + rb0) * p.mask_tk;
-    const int kb_end = CAUSAL ? min(p.mask_tk, ceil_div(min(N, q0 + kFwdBlockM), kSparseBlock)) : p.mask_tk;
+    // wavefront 0 compacts the key blocks the query block keeps into kblocks
+    // (ballot + running count); causal: none past the block's last row
+    const uint8_t* m0 = p.block_mask + ((size_t)(p.mask_heads == 1 ? 0 : bh) * p.mask_tq + qb) * p.mask_tk;
+    const int kb_end = CAUSAL ? min(p.mask_tk, qb + 1) : p.mask_tk;
     int count = 0;
     if (wave_u == 0) {
       for (int base0 = 0; base0 < kb_end; base0 += 64) {
         const int kbk = base0 + lane;
         const int b0 = kbk < kb_end ? (m0[kbk] != 0) : 0;
-        const int b1 = (kbk < kb_end && two) ? (m0[p.mask_tk + kbk] != 0) : 0;
-        const uint64_t keep = __ballot(b0 | b1);
+        const uint64_t keep = __ballot(b0);
         const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0));
-        if (b0 | b1) kblocks[pos] = (uint16_t)(kbk | (b0 << 14) | (b1 << 15));
+        if (b0) kblocks[pos] = (uint16_t)kbk;
         count += __popcll(keep);
       }
     }
@@ -235,16 +241,16 @@ void fa_fwd_kernel(FwdParams p) {
   // first key of tile j (SPARSE: of the j-th tile of the kept blocks)
   auto tile_kv0 = [&](int j) __attribute__((always_inline)) {
     if constexpr (SPARSE)
-      return (((int)kblocks[j >> 1] & 0x3fff) * kSparseBlock) + (j & 1) * T::BN;
+      return ((int)kblocks[j >> 1] * kSparseBlock) + (j & 1) * T::BN;
     else
       return j * T::BN;
   };
   const float c = p.scale_log2;
   auto active = [&](int j) __attribute__((always_inline)) {  // some row of the wave sees the tile
-    if constexpr (SPARSE) {
+    if constexpr (SPARSE) {  // ... in this wavefront's half of it, which holds a key below N
       if (j >= n_tiles) return false;
-      const int e = __builtin_amdgcn_readfirstlane(kblocks[j >> 1]);
-      return ((e >> (14 + (wave_u >> 2))) & 1) && (!CAUSAL || tile_kv0(j) <= wq0 + 31);
+      const int k0 = __builtin_amdgcn_readfirstlane(tile_kv0(j)) + kh;
+      return k0 < N && (!CAUSAL || k0 <= wq0 + 31);
     } else {
       return !CAUSAL || j * T::BN <= wq0 + 31;
     }
@@ -260,16 +266,16 @@ void fa_fwd_kernel(FwdParams p) {
   f32x16_t acc[T::DSUB];
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
-  f32x16_t s[T::NSUB];       // scores of the tile between its QK and its softmax
-  bf16x2_t pw[T::KS_PV][4];  // P̃ of the tile between its softmax and its PV (bf16 pairs)
+  f32x16_t s[NSUB_W];       // scores of the tile between its QK and its softmax
+  bf16x2_t pw[KSPV_W][4];   // P̃ of the tile between its softmax and its PV (bf16 pairs)
 
   // ---- softmax phase of tile j: mask, row max, rescale, P̃ and the sums ------------
   auto softmax = [&](int j, auto clean) __attribute__((always_inline)) {
-    const int kv0 = __builtin_amdgcn_readfirstlane(tile_kv0(j));
-    if (!decltype(clean)::value && ((kv0 + T::BN > N) || (CAUSAL && kv0 + T::BN - 1 > wq0))) {
+    const int kv0 = __builtin_amdgcn_readfirstlane(tile_kv0(j)) + kh;  // first key of the wave's part
+    if (!decltype(clean)::value && ((kv0 + 32 * NSUB_W > N) || (CAUSAL && kv0 + 32 * NSUB_W - 1 > wq0))) {
       const int lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 #pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub)
+      for (int sub = 0; sub < NSUB_W; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + sub * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
@@ -286,7 +292,7 @@ void fa_fwd_kernel(FwdParams p) {
       const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
       float r2[2] = {0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < T::KS_PV; ++kk) {
+      for (int kk = 0; kk < KSPV_W; ++kk) {
         const int h8 = (kk & 1) * 8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -306,7 +312,7 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
 #pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub)
+      for (int sub = 0; sub < NSUB_W; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[sub][r]);
       const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
@@ -329,7 +335,7 @@ void fa_fwd_kernel(FwdParams p) {
 
   // ---- matrix phase: Oᵀ += Vᵀ_j P̃ᵀ_j and Sᵀ_{j+1} = K_{j+1} Qᵀ, MFMAs interleaved ------
   auto qk_step = [&](const unsigned char* kb, int i) __attribute__((always_inline)) {
-    const int kk = i / T::NSUB, sub = i % T::NSUB;
+    const int kk = i / NSUB_W, sub = i % NSUB_W;
     const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + k_rd[kk] + sub * 32 * T::ROW);
     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], s[sub], 0, 0, 0);
   };
@@ -360,8 +366,8 @@ void fa_fwd_kernel(FwdParams p) {
     if (ds == T::DSUB - 1) lb_step(kk);
   };
   auto pv_step = [&](const unsigned char* vb, int i) __attribute__((always_inline)) { pv_mma(i, pv_read(vb, i)); };
-  constexpr int NQK = T::KS_QK * T::NSUB;  // MFMAs of one Sᵀ tile
-  constexpr int NPV = T::KS_PV * T::DSUB;  // MFMAs of one Oᵀ update
+  constexpr int NQK = T::KS_QK * NSUB_W;  // MFMAs of one Sᵀ tile (of the wave's part)
+  constexpr int NPV = KSPV_W * T::DSUB;   // MFMAs of one Oᵀ update
   auto matrix_clean = [&](const unsigned char* vb, const unsigned char* kb) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);  // the matrix-phase wavefront wins issue ties
     // Lane offsets opaque to loop-invariant code motion: addresses are formed
@@ -371,7 +377,7 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int ds = 0; ds < T::DSUB; ++ds) asm volatile("" : "+v"(v_rd[ds]));
 #pragma unroll
-    for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
+    for (int sub = 0; sub < NSUB_W; ++sub) s[sub] = f32x16_t{};
     static_assert(NQK == NPV, "interleave pairs one MFMA of each product");
     // PV(0), PV(1) from the operands read before the barrier, then QK(i) with
     // PV(i+2): the K reads the first QK waits for run under two MFMAs
@@ -398,7 +404,7 @@ void fa_fwd_kernel(FwdParams p) {
   auto matrix = [&](const unsigned char* vb, const unsigned char* kb, bool do_pv, bool do_qk) __attribute__((always_inline)) {
     if (do_qk) {
 #pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
+      for (int sub = 0; sub < NSUB_W; ++sub) s[sub] = f32x16_t{};
 #pragma unroll
       for (int i = 0; i < NQK; ++i) qk_step(kb, i);
     }
@@ -510,7 +516,39 @@ void fa_fwd_kernel(FwdParams p) {
   wait_vmcnt<0>();  // the loads past the last tile write tile buffers too
   block_barrier();
   l = pair_sum(l);
-  const float lbs = pair_sum(lb[0] + lb[1]);
+  float lbs = pair_sum(lb[0] + lb[1]);
+  if constexpr (SPARSE) {
+    // Wavefront w + 4 holds the same rows as w over the other key half of every
+    // tile: it leaves its (m, ℓ, ℓ_b, accumulator) in LDS (K and V buffer w & 3:
+    // every load has landed and every read is done) and w merges the two with ⊕.  Each value
+    // goes to [element][lane], so the stores and loads are conflict-free.
+    const int u = wave_u & 3;
+    float* const xacc = reinterpret_cast<float*>(u == 0 ? k_lds0 : u == 1 ? k_lds1 : u == 2 ? k_lds2 : k_lds3);
+    float* const xrow = reinterpret_cast<float*>(u == 0 ? v_lds0 : u == 1 ? v_lds1 : u == 2 ? v_lds2 : v_lds3);
+    static_assert(T::DSUB * 16 * 64 * 4 <= T::TILE_BYTES, "the accumulator fits one tile buffer");
+    if (grp == 1) {
+#pragma unroll
+      for (int ds = 0; ds < T::DSUB; ++ds)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xacc[(ds * 16 + r) * 64 + lane] = acc[ds][r];
+      xrow[lane] = m;
+      xrow[64 + lane] = l;
+      xrow[128 + lane] = lbs;
+    }
+    block_barrier();
+    if (grp == 1) return;  // no barrier follows
+    const float m2 = xrow[lane];
+    const float mm = fmaxf(m, m2);  // −∞: neither half of the row saw a key
+    const float f1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mm) * c);
+    const float f2 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mm) * c);
+    l = l * f1 + xrow[64 + lane] * f2;
+    lbs = lbs * f1 + xrow[128 + lane] * f2;
+#pragma unroll
+    for (int ds = 0; ds < T::DSUB; ++ds)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ds][r] = acc[ds][r] * f1 + xacc[(ds * 16 + r) * 64 + lane] * f2;
+    m = mm;
+  }
   const float inv = (SPARSE && lbs == 0.f) ? 0.f : 1.f / lbs;  // SPARSE: a row with no key writes O = 0, L = −∞
   constexpr int SROW = 2 * D + 16;  // padded row stride of the staging tile (bytes)
   static_assert(32 * SROW <= T::TILE_BYTES, "a wavefront's rows fit one tile buffer");
