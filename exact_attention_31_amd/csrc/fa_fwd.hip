@@ -106,7 +106,15 @@ struct Tile {
 // 8 XCDs; with xcd_remap each XCD receives whole heads (so a head's K/V stays
 // in one L2), and inside an XCD's share the heaviest query blocks (the last
 // ones, for causal) are dispatched first (longest-processing-time-first,
-// [15-779 L5] §6.2).
+// [15-779 L5] §6.2): r is the rank of the block in that order.
+// PAIR (kernels that fit two workgroups on a CU): when an XCD's share fits its
+// CUs at once — C < share ≤ 2C, C = kCusPerXcd — the first C workgroups take
+// one CU each and workgroup C + k lands on the CU of workgroup k, so the order
+// is arranged for that: the share's heaviest C − P blocks (P = share − C) get
+// CUs of their own, and the next P are each paired with one of the P lightest,
+// heaviest with lightest, which evens out the work per CU (causal blocks differ
+// up to N/256-fold in length).  Only the order changes, not any result.
+template <bool PAIR>
 __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
   const int x = blockIdx.x;
   const int total = p.BH * p.n_qblk;
@@ -115,8 +123,15 @@ __device__ inline void decode_work(const FwdParams& p, int& bh, int& qb) {
     const int heads_per_xcd = per_xcd / p.n_qblk;
     const int xcd = x & 7;
     const int local = x >> 3;
-    bh = xcd * heads_per_xcd + local % heads_per_xcd;
-    qb = p.n_qblk - 1 - local / heads_per_xcd;
+    int r = local;
+    if (PAIR && per_xcd > kCusPerXcd && per_xcd <= 2 * kCusPerXcd) {
+      const int P = per_xcd - kCusPerXcd;
+      r = local < P ? (kCusPerXcd - P) + local                  // paired, heavier of the two
+          : local < kCusPerXcd ? local - P                      // alone on its CU: the heaviest
+          : per_xcd - 1 - (local - kCusPerXcd);                 // paired, lighter of the two
+    }
+    bh = xcd * heads_per_xcd + r % heads_per_xcd;
+    qb = p.n_qblk - 1 - r / heads_per_xcd;
   } else {
     bh = x % p.BH;
     qb = p.n_qblk - 1 - x / p.BH;
@@ -159,7 +174,7 @@ void fa_fwd_kernel(FwdParams p) {
   __shared__ uint16_t kblocks[SPARSE ? kSparseMaxBlocks : 1];
 
   int bh, qb;
-  decode_work(p, bh, qb);
+  decode_work<D == 64 && CAUSAL && !SPARSE>(p, bh, qb);  // the two-workgroups-per-CU form
   const int N = p.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

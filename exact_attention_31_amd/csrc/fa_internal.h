@@ -14,6 +14,9 @@ namespace fa {
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBlockM = 32 * kFwdWaves;
+// Compute units per XCD of the MI355X (256 CUs in 8 XCDs); it only steers the
+// order in which workgroups are handed out, never a result.
+constexpr int kCusPerXcd = 32;
 
 __host__ __device__ constexpr int fwd_block_n(int) { return 64; }
 
