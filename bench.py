@@ -287,7 +287,7 @@ def copy_reference(torch, dev, args):
 def time_gqa(torch, fa, synth, dev, args, traffic):
     """The grouped-query decode (32 query heads over 8 K/V heads, full lengths), timed
     on its own after the step: W warm-up calls, then K calls, each between HIP events."""
-    wg = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s32"]
+    wg = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s8"]
     print(f"[bench] generating inputs: {wg.name}", file=sys.stderr, flush=True)
     qg = synth.make_decode_q(wg).to(dev)
     kg, vg = synth.make_decode_kv(wg, device=dev)

@@ -64,10 +64,10 @@ __global__ __launch_bounds__(256) void fa_fp8_quantize_kernel(Fp8QuantParams p) 
   const int row = t * kFp8Block + r;
   const uint16_t* src = tensor == 0 ? p.q : (tensor == 1 ? p.k : p.v);
   const size_t roff = ((size_t)bh * p.N + row) * kFp8D + 32 * c4;
-  u32x4_t w[4];  // each input byte is read once: nontemporal loads, which displace no cached line
+  u32x4_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    w[i] = row < p.N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + roff) + i) : u32x4_t{0, 0, 0, 0};
+    w[i] = row < p.N ? reinterpret_cast<const u32x4_t*>(src + roff)[i] : u32x4_t{0, 0, 0, 0};
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i)

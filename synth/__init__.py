@@ -72,8 +72,8 @@ WORKLOADS = [
 # Grouped-query decode (Llama-3-8B's 32 query heads over 8 K/V heads), the
 # widening of the decode workload above to shared K/V heads.
 EXTRA_WORKLOADS = [
-    Workload("decode_gqa_b16hq32hkv8_lkv32768_d128_s32", "decode", 16, 32, 1, 128, False,
-             lkv=32768, num_splits=32, wid=6, hkv=8),
+    Workload("decode_gqa_b16hq32hkv8_lkv32768_d128_s8", "decode", 16, 32, 1, 128, False,
+             lkv=32768, num_splits=8, wid=6, hkv=8),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

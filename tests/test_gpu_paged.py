@@ -105,7 +105,7 @@ def test_paged_table_entries_are_clamped_into_the_pool():
 def test_paged_full_size_matches_contiguous():
     """The grouped-query bench workload (B16, 32 over 8 heads, 32768 keys, d128) in
     64-key pages under a seeded permutation: bit-identical to the contiguous call."""
-    w = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s32"]
+    w = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s8"]
     _say("[case] paged full size", w.name)
     q = synth.make_decode_q(w).cuda()
     k, v = synth.make_decode_kv(w, device="cuda")

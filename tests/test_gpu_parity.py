@@ -329,9 +329,10 @@ def test_decode_is_decode_gqa_with_one_query_per_kv_head():
 
 
 def test_decode_gqa_full_size_sampled_heads():
-    """B16 Hq32 Hkv8 Lmax 32768 d128, 64 splits, ragged lengths (one full, one of a
-    single key); the oracle recomputes 8 query heads of 4 sequences."""
-    w = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s32"]
+    """B16 Hq32 Hkv8 Lmax 32768 d128 at the workload's split count, ragged lengths
+    (one full, one of a single key); the oracle recomputes 8 query heads of 4
+    sequences."""
+    w = synth.BY_NAME["decode_gqa_b16hq32hkv8_lkv32768_d128_s8"]
     _say("[case] workload", w.name, "(ragged lengths)")
     q = synth.make_decode_q(w)
     k, v = synth.make_decode_kv(w, device="cuda")
