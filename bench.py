@@ -453,7 +453,8 @@ def time_fp8(torch, fa, synth, dev, args):
     """The FP8 prefill on the prefill workload and on the long non-causal one:
     fa_fwd_fp8 on operands fa_quantize_fp8 wrote beforehand, interleaved with the
     bf16 fa_fwd on the same inputs, W + K calls each between HIP events; the
-    quantising pass is timed on its own."""
+    quantising pass is timed on its own.  ``warm`` times K calls of each back to
+    back as well."""
     res = {}
     for wname in ("llama3_8b_causal_b1h32n4096d128_kboost", "long_noncausal_b1h16n16384d128"):
         w = synth.BY_NAME[wname]
@@ -480,11 +481,28 @@ def time_fp8(torch, fa, synth, dev, args):
             e[5].record()
         torch.cuda.synchronize()
         f8, bf, qz = (sum(e[a].elapsed_time(e[a + 1]) for e in ev) / len(ev) for a in (0, 2, 4))
+        # each call also K times back to back (warm caches, the same power state for both)
+        warm = {}
+        for label, call in (("fp8", lambda: fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale,
+                                                           causal=w.causal, out=o, lse=lse)),
+                            ("bf16", lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse))):
+            call()
+            torch.cuda.synchronize()
+            evw = [[Event() for _ in range(2)] for _ in range(args.steps)]
+            for e in evw:
+                e[0].record()
+                call()
+                e[1].record()
+            torch.cuda.synchronize()
+            warm[label] = sum(e[0].elapsed_time(e[1]) for e in evw) / len(evw)
         flops = synth.prefill_flops(w)
         tf = flops / (f8 * 1e-3) / 1e12
         res[w.name] = {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(f8, 4),
                        "frac_mfma_fp8_peak": round(tf / MFMA_FP8_PEAK_TFLOPS, 4), "bf16_ms": round(bf, 4),
-                       "speedup_vs_bf16": round(bf / f8, 3), "quantize_ms": round(qz, 4)}
+                       "speedup_vs_bf16": round(bf / f8, 3), "quantize_ms": round(qz, 4),
+                       "warm": {"ms": round(warm["fp8"], 4), "bf16_ms": round(warm["bf16"], 4),
+                                "speedup_vs_bf16": round(warm["bf16"] / warm["fp8"], 3),
+                                "note": f"{args.steps} calls of each back to back"}}
     return res
 
 

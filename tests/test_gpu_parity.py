@@ -176,6 +176,26 @@ def test_many_blocks_ragged(n, causal, d):
     _check(f"H32 N={n} causal={causal} d={d} (sampled)", o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl)
 
 
+@pytest.mark.parametrize("B,H,n", [(8, 12, 1000), (4, 12, 2048), (10, 12, 1024), (3, 12, 1000)])
+def test_cu_pairing_order(B, H, n):
+    """d = 64 causal grids that fit the CUs at once, where workgroups are handed out
+    heaviest-alone / heaviest-with-lightest (B8 H12 N1000: a ragged last block; B4 H12
+    N2048: eight blocks a head; B10 H12: 60 workgroups an XCD), and one whose grid the
+    XCD remap does not take (B3 H12 N1000: 18 workgroups an XCD, not whole heads):
+    every block of every head against the oracle on sampled rows."""
+    w = W[1].with_(B=B, H=H, N=n, wid=70 + n + B)
+    _say("[case] CU pairing order", B, H, n)
+    q, k, v = synth.make_prefill(w)
+    o, lse = _run_fwd(q, k, v, w.scale, True)
+    rng = np.random.default_rng(n + B)
+    edges = [r for blk in range(0, n, 256) for r in (blk, blk + 31, blk + 224, blk + 255) if r < n]
+    rows = np.unique(np.concatenate([edges, [n - 1], rng.choice(n, 24, replace=False)]))
+    for b in range(B):
+        ro, rl = attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], w.scale, True, rows=rows)
+        _check(f"B{B} H{H} N={n} d64 causal, batch {b} (sampled)", o[b:b + 1][:, :, rows], lse[b:b + 1][:, :, rows],
+               ro, rl)
+
+
 def test_decode_full_size_sampled_heads():
     """B16 H32 Lkv 32768 d128, 64 splits; the oracle recomputes 8 heads unsplit."""
     w = W[4]
