@@ -460,31 +460,31 @@ def time_fp8(torch, fa, synth, dev, args):
         w = synth.BY_NAME[wname]
         print(f"[bench] fp8: {w.name}", file=sys.stderr, flush=True)
         q, k, v = (t.to(dev) for t in synth.make_prefill(w))
-        packed = fa.fa_quantize_fp8(q, k, v)
+        packed = fa.fa_quantize_fp8(q, k, v, scale=w.scale)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         for _ in range(args.warmup):
-            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, causal=w.causal, out=o, lse=lse)
             fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
-            fa.fa_quantize_fp8(q, k, v, packed=packed)
+            fa.fa_quantize_fp8(q, k, v, scale=w.scale, packed=packed)
         torch.cuda.synchronize()
         ev = [[Event() for _ in range(6)] for _ in range(args.steps)]
         for e in ev:
             e[0].record()
-            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale, causal=w.causal, out=o, lse=lse)
+            fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, causal=w.causal, out=o, lse=lse)
             e[1].record()
             e[2].record()
             fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
             e[3].record()
             e[4].record()
-            fa.fa_quantize_fp8(q, k, v, packed=packed)
+            fa.fa_quantize_fp8(q, k, v, scale=w.scale, packed=packed)
             e[5].record()
         torch.cuda.synchronize()
         f8, bf, qz = (sum(e[a].elapsed_time(e[a + 1]) for e in ev) / len(ev) for a in (0, 2, 4))
         # each call also K times back to back (warm caches, the same power state for both)
         warm = {}
-        for label, call in (("fp8", lambda: fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, scale=w.scale,
-                                                           causal=w.causal, out=o, lse=lse)),
+        for label, call in (("fp8", lambda: fa.fa_fwd_fp8(packed, w.B, w.H, w.N, w.d, causal=w.causal, out=o,
+                                                           lse=lse)),
                             ("bf16", lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse))):
             call()
             torch.cuda.synchronize()

@@ -80,9 +80,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_paged.restype = i
     lib.fa_fp8_packed_bytes.argtypes = [i, i, i, i]
     lib.fa_fp8_packed_bytes.restype = sz
-    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     lib.fa_quantize_fp8.restype = i
-    lib.fa_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
@@ -509,10 +509,11 @@ def fa_fp8_packed_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_fp8_packed_bytes(B, H, N, d))
 
 
-def fa_quantize_fp8(q, k, v, packed=None):
+def fa_quantize_fp8(q, k, v, scale=None, packed=None):
     """Block-wise FP8 (E4M3) quantisation of bf16 q, k, v [B, H, N, 128] into the
-    packed operand buffer of fa_fwd_fp8 (a uint8 tensor; allocated when not given).
-    Runs asynchronously on the current stream; returns the buffer."""
+    packed operand buffer of fa_fwd_fp8 (a uint8 tensor; allocated when not given),
+    for the softmax scale ``scale`` (default fp32(1/sqrt(d))), which is folded into
+    Q.  Runs asynchronously on the current stream; returns the buffer."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, 4)
@@ -521,28 +522,28 @@ def fa_quantize_fp8(q, k, v, packed=None):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     need = fa_fp8_packed_bytes(B, H, N, d)
     if packed is None:
         packed = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     pbytes = _check_buffer(packed, "packed", q.device)
-    st = load_library().fa_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, packed.data_ptr(),
-                                        pbytes, _stream_ptr(q.device))
+    st = load_library().fa_quantize_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, float(scale),
+                                        packed.data_ptr(), pbytes, _stream_ptr(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_quantize_fp8")
     return packed
 
 
-def fa_fwd_fp8(packed, B, H, N, d=128, scale=None, causal=False, out=None, lse=None):
-    """Attention forward on the FP8 operands fa_quantize_fp8 wrote: returns
-    (o bf16 [B, H, N, d], lse fp32 [B, H, N]).  ``scale`` defaults to fp32(1/sqrt(d))."""
+def fa_fwd_fp8(packed, B, H, N, d=128, causal=False, out=None, lse=None):
+    """Attention forward on the FP8 operands fa_quantize_fp8 wrote (for the
+    softmax scale it was given): returns (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
     torch = _torch()
     if not isinstance(packed, torch.Tensor) or packed.dtype != torch.uint8:
         raise TypeError("packed must be a uint8 tensor")
     if packed.device.type != "cuda":
         raise ValueError(f"packed must be on a ROCm device, got {packed.device}")
     pbytes = _check_buffer(packed, "packed", packed.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=packed.device)
     _check_out(out, "out", (B, H, N, d), torch.bfloat16, packed.device)
@@ -550,7 +551,7 @@ def fa_fwd_fp8(packed, B, H, N, d=128, scale=None, causal=False, out=None, lse=N
         lse = torch.empty((B, H, N), dtype=torch.float32, device=packed.device)
     _check_out(lse, "lse", (B, H, N), torch.float32, packed.device)
     st = load_library().fa_fwd_fp8(packed.data_ptr(), pbytes, out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                                   float(scale), int(bool(causal)), _stream_ptr(packed.device))
+                                   int(bool(causal)), _stream_ptr(packed.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
     return out, lse

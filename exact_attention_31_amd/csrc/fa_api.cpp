@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 static_assert(FA_DECODE_NOALLOC_SCRATCH_BYTES == fa::kDecodeScratchBytes, "the header states the scratch size");
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -395,11 +395,12 @@ size_t fa_fp8_packed_bytes(int B, int H, int N, int d) {
   return fa::fp8_layout(B, H, N, d).total;
 }
 
-fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, void* packed,
-                          size_t packed_bytes, void* stream) {
+fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                          void* packed, size_t packed_bytes, void* stream) {
   if (!q || !k || !v || !packed) return FA_ERR_NULL;
   const fa_status sh = fp8_shape(B, H, N, d);
   if (sh != FA_OK) return sh;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed)) return FA_ERR_ALIGN;
   const fa::Fp8Layout L = fa::fp8_layout(B, H, N, d);
   if (packed_bytes < L.total) return FA_ERR_WORKSPACE;
@@ -415,16 +416,16 @@ fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, in
   p.BH = B * H;
   p.N = N;
   p.T = fa::ceil_div(N, fa::kFp8Block);
+  p.qmul = scale * kLog2e;
   if (fa::launch_fp8_quantize(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }
 
 fa_status fa_fwd_fp8(const void* packed, size_t packed_bytes, void* o, float* lse, int B, int H, int N, int d,
-                     float scale, int causal, void* stream) {
+                     int causal, void* stream) {
   if (!packed || !o || !lse) return FA_ERR_NULL;
   const fa_status sh = fp8_shape(B, H, N, d);
   if (sh != FA_OK) return sh;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_VALUE;
   const fa::Fp8Layout L = fa::fp8_layout(B, H, N, d);
   if (packed_bytes < L.total) return FA_ERR_WORKSPACE;
   if (!aligned16(packed) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
@@ -442,8 +443,6 @@ fa_status fa_fwd_fp8(const void* packed, size_t packed_bytes, void* o, float* ls
   p.n_qblk = fa::ceil_div(N, fa::kFwdBlockM);
   const long long total = (long long)p.BH * p.n_qblk;
   p.xcd_remap = (total % 8 == 0) && ((total / 8) % p.n_qblk == 0);
-  p.scale = scale;
-  p.scale_log2 = scale * kLog2e;
   if (fa::launch_fwd_fp8(p, causal ? 1 : 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }

@@ -65,6 +65,7 @@ struct Fp8QuantParams {
   int BH;
   int N;
   int T;
+  float qmul;  // c = scale·log2(e): Q is quantised as c·Q
 };
 
 struct Fp8FwdParams {
@@ -77,8 +78,6 @@ struct Fp8FwdParams {
   int T;
   int n_qblk;
   int xcd_remap;
-  float scale;
-  float scale_log2;
 };
 
 hipError_t launch_fp8_quantize(const Fp8QuantParams& p, hipStream_t stream);

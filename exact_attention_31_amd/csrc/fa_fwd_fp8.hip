@@ -68,13 +68,16 @@ __global__ __launch_bounds__(256) void fa_fp8_quantize_kernel(Fp8QuantParams p) 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     w[i] = row < p.N ? reinterpret_cast<const u32x4_t*>(src + roff)[i] : u32x4_t{0, 0, 0, 0};
+  // Q is quantised as c·Q (c = scale·log2 e): the logits of the forward then come
+  // out of the first product in base 2 (one fp32 rounding per element here)
+  const float mul = tensor == 0 ? p.qmul : 1.f;
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      x[8 * i + 2 * h] = __uint_as_float(w[i][h] << 16);
-      x[8 * i + 2 * h + 1] = __uint_as_float(w[i][h] & 0xffff0000u);
+      x[8 * i + 2 * h] = __uint_as_float(w[i][h] << 16) * mul;
+      x[8 * i + 2 * h + 1] = __uint_as_float(w[i][h] & 0xffff0000u) * mul;
     }
   float amax = 0.f;
 #pragma unroll
@@ -227,12 +230,16 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
     qf[kb] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  const float c = p.scale_log2;
   auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * T::BN <= wq0 + 31; };
   auto kscale = [&](int j) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(ksc[j]); };
   auto vscale = [&](int j) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(vsc[j]); };
 
-  float m = -INFINITY, l = 0.f;
+  // m: the reference max of this lane's row, base 2.  The first logit instruction
+  // of a tile starts from −mo (its accumulator input), mo the reference max when
+  // the tile's products are issued (0 while m is −∞): the logits come out as
+  // t − mo, so while m = mo, P̃ = 2^(t − m) is one exp2 of them.
+  float m = -INFINITY, l = 0.f, mo = 0.f;
+  f32x16_t moff = {};  // −mo in every element
   f32x16_t acc[T::DSUB];
 #pragma unroll
   for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] = f32x16_t{};
@@ -253,20 +260,20 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
           if (key > lim) s[sub][r] = -INFINITY;
         }
     }
-    // P̃ against the reference max in fp32, and the lane's sum over each 32-key
-    // sub-tile (the E4M3 conversion follows in the matrix phase, `convert`).
-    // The lane's sum bounds each of its elements, so a sum at most 2^48 proves
-    // that no row outgrew m by more.
+    // P̃ = 2^(s + off) in fp32 (off = 0 while m = mo), and the lane's sum over
+    // each 32-key sub-tile (the E4M3 conversion follows in the matrix phase,
+    // `convert`).  The lane's sum bounds each of its elements, so a sum at most
+    // 2^48 proves that no row outgrew m by more.
     float rs;
-    auto exps = [&]() __attribute__((always_inline)) {
-      const float mc = m * c;
+    auto exps = [&](auto with_off, float off) __attribute__((always_inline)) {
 #pragma unroll
       for (int sub = 0; sub < T::NSUB; ++sub) {
         float r2[2];
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) pe[sub][r + t] = __builtin_amdgcn_exp2f(fmaf(s[sub][r + t], c, -mc));
+          for (int t = 0; t < 4; ++t)
+            pe[sub][r + t] = __builtin_amdgcn_exp2f(decltype(with_off)::value ? s[sub][r + t] + off : s[sub][r + t]);
           const float q4 = (pe[sub][r] + pe[sub][r + 1]) + (pe[sub][r + 2] + pe[sub][r + 3]);
           r2[(r >> 2) & 1] = r < 8 ? q4 : r2[(r >> 2) & 1] + q4;
         }
@@ -274,8 +281,8 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
       }
       rs = rsub[0] + rsub[1];
     };
-    exps();
-    if (__any(!(rs <= kFp8SumBound))) {  // also taken for inf / NaN sums (first tile: m = −∞)
+    exps(std::false_type{}, 0.f);
+    if (__any(!(rs <= kFp8SumBound) || m == -INFINITY)) {  // also taken for inf / NaN sums and the first tile
       float mx[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
@@ -283,15 +290,18 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
       for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[sub][r]);
-      const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-      if (__any((mt - m) * c > kFp8RescaleLog2)) {
+      const float mt = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) + mo;  // the tile's row max, base 2
+      if (__any(mt - m > kFp8RescaleLog2)) {
         const float m_new = fmaxf(m, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = −∞ (ℓ and acc are 0 then)
         l *= alpha;
 #pragma unroll
         for (int ds = 0; ds < T::DSUB; ++ds) acc[ds] *= alpha;
         m = m_new;
-        exps();
+        exps(std::true_type{}, mo - m);
+        mo = m;  // the next tiles start from the new max
+#pragma unroll
+        for (int e = 0; e < 16; ++e) moff[e] = -m;
       }
     }
     l += rs;
@@ -310,7 +320,8 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   };
   auto qk_step = [&](const unsigned char* kb, int i, int kse) __attribute__((always_inline)) {
     const int sub = i / T::KB, kbk = i % T::KB;
-    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop(kb, i), qf[kbk], s[sub], 0, 0, 0, kse, 0, qse);
+    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop(kb, i), qf[kbk], kbk == 0 ? moff : s[sub], 0, 0, 0, kse,
+                                                             0, qse);
   };
   auto pv_step = [&](const unsigned char* vb, int ds, int vse) __attribute__((always_inline)) {
     acc[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop(vb, ds), pb, acc[ds], 0, 0, 0, vse, 0, psc);
@@ -350,10 +361,6 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   auto matrix = [&](const unsigned char* vb, const unsigned char* kb, bool do_pv, bool do_qk, int vse, int kse)
       __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    if (do_qk) {
-#pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub) s[sub] = f32x16_t{};
-    }
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (do_qk) qk_step(kb, i, kse);
@@ -455,7 +462,7 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   for (int it = 0; it < 32 / RPI; ++it)
     if (wq0 + it * RPI + rr0 < N)
       *reinterpret_cast<u32x4_t*>(p.o + obase + (size_t)(wq0 + it * RPI + rr0) * kFp8D + cc * 8) = ow[it];
-  if (q_row < N && g == 0) p.lse[(size_t)bh * N + q_row] = m * p.scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
+  if (q_row < N && g == 0) p.lse[(size_t)bh * N + q_row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
 template <bool CAUSAL>

@@ -264,11 +264,15 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
 /* ---- FP8 form of the prefill ([cicada] §4.4.1: block-wise quantisation) ----
  *
  * fa_quantize_fp8 turns bf16 Q, K, V [B, H, N, d] (d = 128) into the packed FP8
- * operand buffer that fa_fwd_fp8 reads.  Every run of 64 rows of one (b, h)
- * slice of each tensor gets its own scale s = 2^e, e the smallest integer with
- * (largest |x| of the block) ≤ 448·2^e, clamped to [−127, 127] (e = 0 for an
- * all-zero block); each element becomes the OCP E4M3FN value nearest to x/s
- * (ties to even).  The buffer holds, each section 256-byte aligned and in this
+ * operand buffer that fa_fwd_fp8 reads, for the softmax scale `scale` (finite,
+ * > 0; fp32(1/√d) is the usual one).  Q is taken as c·Q, c = scale·log2(e)
+ * (both factors in fp32, product rounded to fp32, each element's product
+ * rounded to fp32): the softmax scale, in base 2, travels in Q's codes, so the
+ * forward's logits come out of its first product in base 2.  Every run of 64
+ * rows of one (b, h) slice of each tensor (c·Q, K, V) gets its own scale
+ * s = 2^e, e the smallest integer with (largest |x| of the block) ≤ 448·2^e,
+ * clamped to [−127, 127] (e = 0 for an all-zero block); each element becomes
+ * the OCP E4M3FN value nearest to x/s (ties to even).  The buffer holds, each section 256-byte aligned and in this
  * order, with T = ⌈N/64⌉: the codes of Q and of K ([B·H][N][d] bytes each); the
  * codes of V one 64-key tile at a time, transposed, [B·H][T][d][64] bytes, the
  * 64 keys of a row in the order that the forward's second product reads them
@@ -277,9 +281,10 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
  * bytes e + 127, [B·H][T] each.  packed_bytes must be at least
  * fa_fp8_packed_bytes(B, H, N, d); the buffer may not overlap q, k or v.
  *
- * fa_fwd_fp8 computes O [B, H, N, d] (bf16) and L [B, H, N] (fp32) of the
- * attention these operands define, exact attention of the dequantised
- * Q̂ = s·q₈, K̂, V̂ with scale and causal as for fa_fwd, except that the
+ * fa_fwd_fp8 computes O [B, H, N, d] (bf16) and L [B, H, N] (fp32, natural log)
+ * of the attention these operands define, exact attention of the dequantised
+ * Q̂' = s·q₈' (≈ c·Q), K̂, V̂ with base-2 logits Q̂'K̂ᵀ (the scale the buffer
+ * was quantised for) and causal as for fa_fwd, except that the
  * probabilities enter the second product rounded to E4M3, block-quantised in
  * turn: the probabilities of a row over each aligned half (32 keys) of a
  * 64-key tile are divided by a power of two 2^σ no larger than 2^-7 times their
@@ -291,10 +296,10 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
  * for the same B, H, N.  Status codes as for fa_fwd, FA_ERR_UNSUPPORTED for
  * d ≠ 128, FA_ERR_WORKSPACE for a short buffer. */
 size_t fa_fp8_packed_bytes(int B, int H, int N, int d);
-fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, void* packed,
-                          size_t packed_bytes, void* stream);
+fa_status fa_quantize_fp8(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                          void* packed, size_t packed_bytes, void* stream);
 fa_status fa_fwd_fp8(const void* packed, size_t packed_bytes, void* o, float* lse, int B, int H, int N, int d,
-                     float scale, int causal, void* stream);
+                     int causal, void* stream);
 
 /* Number of (query block, key tile) pairs fa_fwd processes for one (b, h),
  * with the block and tile sizes of fa_fwd_tile_shape: ⌈N/BM⌉·⌈N/BN⌉ when not
@@ -312,7 +317,8 @@ fa_status fa_fwd_tile_shape(int d, int* block_m, int* block_n);
 const char* fa_status_str(int status);
 
 /* ABI version of this header (bumped on incompatible changes; 2: fa_fwd_fp8
- * takes the packed buffer's size). */
+ * takes the packed buffer's size; 3: the softmax scale moved from fa_fwd_fp8 to
+ * fa_quantize_fp8, which folds it into Q). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

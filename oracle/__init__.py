@@ -33,7 +33,7 @@ from .ref import (
     masked_probs,
 )
 from .compare import bf16_half_ulp, o_excess, check_prefill, check_decode, bwd_allowance, check_bwd
-from .fp8 import e4m3_round, quantize_blocks, dequantize_blocks, attention_fp8_ref
+from .fp8 import e4m3_round, quantize_blocks, dequantize_blocks, attention_fp8_ref, prescale_q
 
 __all__ = [
     "scores",
@@ -55,4 +55,5 @@ __all__ = [
     "quantize_blocks",
     "dequantize_blocks",
     "attention_fp8_ref",
+    "prescale_q",
 ]

@@ -23,10 +23,18 @@ Readings taken here (the page fixes neither the format nor the block shapes):
 * Blocks are runs of 64 consecutive rows of one (batch, head) slice, all d
   columns together, for Q, K and V alike (the kernel's key tile, and a
   quarter of its query block).
+* The softmax scale enters through Q: before Q is quantised every element is
+  multiplied by c = scale·log₂e (the two factors in fp32, their product rounded
+  to fp32, then the element's fp32 product rounded once, ``prescale_q``), so the
+  logits q̂'·k̂ of the quantised operands are already in base 2 and the
+  probabilities are 2^(q̂'·k̂ − m) with no multiply of their own.  Softmax is
+  unchanged by where the scale is applied; the rounding differs (c·q is
+  quantised, not q).  K and V are quantised as they are.
 * The attention that FP8 inputs define is exact attention of the dequantised
-  Q̂ = s·q₈, K̂, V̂ (``attention_fp8_ref``).  Rounding the probabilities to FP8
-  before the second product is a step of the kernel, not of this definition; its
-  error is bounded separately.
+  Q̂' = s·q₈' (q₈' the codes of c·Q), K̂, V̂ with base-2 logits q̂'·k̂, i.e. with
+  scale ln 2 (``attention_fp8_ref``).  Rounding the probabilities to FP8 before
+  the second product is a step of the kernel, not of this definition; its error
+  is bounded separately.
 """
 
 import numpy as np
@@ -34,6 +42,8 @@ import numpy as np
 from .ref import as_f64, attention_ref
 
 E4M3_MAX = 448.0
+LN2 = float(np.log(2.0))
+LOG2E_F32 = np.float32(1.4426950408889634)  # log2(e) rounded to fp32
 _MIN_NORMAL_EXP = -6   # smallest normal: 2^-6
 _MANT_BITS = 3
 
@@ -108,15 +118,29 @@ def dequantize_blocks(x8, scales, block_rows):
     return x8 * rep[..., None]
 
 
+def logit_scale_f32(scale):
+    """c = scale·log2(e) as the library forms it: scale and log2(e) in fp32, their
+    product rounded to fp32."""
+    return np.float32(np.float32(scale) * LOG2E_F32)
+
+
+def prescale_q(q, scale):
+    """Q as the FP8 quantising pass takes it: every element (exact in fp32) times
+    c = logit_scale_f32(scale), the product rounded to fp32.  Returns float64."""
+    q32 = as_f64(q).astype(np.float32)
+    return (q32 * logit_scale_f32(scale)).astype(np.float64)
+
+
 def attention_fp8_ref(q, k, v, scale, causal, q_block=64, kv_block=64, rows=None):
-    """Exact attention of block-quantised inputs: Q, K and V are quantised with
-    quantize_blocks (Q in blocks of q_block rows, K and V in blocks of kv_block
-    keys), dequantised, and fed to attention_ref.  Returns (O, LSE) as float64
-    like attention_ref, for the query rows ``rows`` (all by default)."""
-    qh = dequantize_blocks(*quantize_blocks(q, q_block), q_block)
+    """Exact attention of block-quantised inputs: c·Q (``prescale_q``), K and V
+    are quantised with quantize_blocks (Q in blocks of q_block rows, K and V in
+    blocks of kv_block keys), dequantised, and fed to attention_ref with the
+    base-2 logits of c·Q, i.e. scale ln 2.  Returns (O, LSE) as float64 like
+    attention_ref, for the query rows ``rows`` (all by default)."""
+    qh = dequantize_blocks(*quantize_blocks(prescale_q(q, scale), q_block), q_block)
     kh = dequantize_blocks(*quantize_blocks(k, kv_block), kv_block)
     vh = dequantize_blocks(*quantize_blocks(v, kv_block), kv_block)
-    return attention_ref(qh, kh, vh, scale, causal, rows=rows)
+    return attention_ref(qh, kh, vh, LN2, causal, rows=rows)
 
 
 def _block_mass(p, seen, av, pblock):
@@ -151,7 +175,7 @@ def fp8_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=32):
     Returns (O_ref, L_ref, allowance) as float64 [B, H, R, d], [B, H, R],
     [B, H, R, d] for the query rows ``rows`` (all by default)."""
     from .ref import scores, safe_softmax
-    qh = dequantize_blocks(*quantize_blocks(q, block), block)
+    qh = dequantize_blocks(*quantize_blocks(prescale_q(q, scale), block), block)
     kh = dequantize_blocks(*quantize_blocks(k, block), block)
     vh = dequantize_blocks(*quantize_blocks(v, block), block)
     B, H, N, _ = qh.shape
@@ -161,7 +185,7 @@ def fp8_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=32):
     allow = np.empty_like(o)
     for b in range(B):
         for h in range(H):
-            s = scores(qh[b, h][rows], kh[b, h], scale, causal, rows)
+            s = scores(qh[b, h][rows], kh[b, h], LN2, causal, rows)
             p, m, l = safe_softmax(s)
             o[b, h] = p @ vh[b, h]
             lse[b, h] = m + np.log(l)
@@ -266,13 +290,14 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
                    group=FP8_GROUP_ROWS, tile=FP8_KEY_TILE, threshold=FP8_RESCALE_LOG2, pblock=FP8_P_BLOCK):
     """The FP8 forward's step, carried out in fp64 (a model, not the definition).
 
-    Q, K, V are quantised block-wise (``quantize_blocks``, blocks of ``block``
-    rows).  Per query row the keys are taken ``tile`` at a time, in order
-    ([15-779 L5] §5.1):
+    c·Q (``prescale_q``), K and V are quantised block-wise (``quantize_blocks``,
+    blocks of ``block`` rows).  Per query row the keys are taken ``tile`` at a
+    time, in order ([15-779 L5] §5.1):
 
-    * logits: Q₈·K₈ᵀ over the head dimension by ``mma_runs`` (two instructions
-      of 64, the second accumulating on the first), times the two block scales;
-      base-2 units t = scale·log2(e)·logit; causal: keys after the row masked;
+    * logits: Q₈'·K₈ᵀ over the head dimension by ``mma_runs`` (two instructions
+      of 64, the second accumulating on the first), times the two block scales:
+      base-2 units t already (c is in the codes of Q); causal: keys after the
+      row masked;
     * a reference max M per row, −∞ at first; the first tile sets M to the
       row's max over it; at a later tile, if any row of the row's group
       (``group`` consecutive rows, aligned) has a tile max more than
@@ -290,8 +315,10 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
     Besides the result, the model bounds how far a kernel doing the same with
     fp32 logits, exp2 and additions can lie from it:
     * ``ex`` per element: |log2 P̃_kernel − log2 P̃| from the fp32 additions of
-      the logit's run sums (γ_9 per instruction), the max's own logit, the
-      roundings of the exponent's arguments and 2^-21 for exp2;
+      the logit's run sums and of the −M the first instruction starts from (the
+      kernel subtracts the reference max there, as its accumulator input; γ_9
+      per instruction), the max's own logit, the roundings of the exponent's
+      arguments (a tile that moves M re-offsets them) and 2^-21 for exp2;
     * ``amb``: a P̃ whose interval P̃·2^(±ex) straddles an E4M3 rounding
       boundary may round either way in the kernel; its largest possible change
       times |v̂|, plus — where the other rounding's product could reach its
@@ -321,13 +348,12 @@ def fp8_step_model(q, k, v, scale, causal, rows=None, block=64, round_p=True, mm
 
 def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, tile, threshold, pblock):
     import torch
-    q8, qs = quantize_blocks(q, block)
+    q8, qs = quantize_blocks(prescale_q(q, scale), block)
     k8, ks = quantize_blocks(k, block)
     v8, vs = quantize_blocks(v, block)
     assert tile == block and tile % MMA_RUN == 0 and tile % pblock == 0 and pblock % MMA_RUN == 0
     B, H, N, d = q8.shape
     assert d % 64 == 0
-    c = scale * np.log2(np.e)
     g9 = _gamma(9)
     grp = _groups_for(rows, N, group)
     allrows = (grp[:, None] * group + np.arange(group)[None, :]).reshape(-1)
@@ -373,8 +399,11 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                 codes = runs.sum(1).numpy()
                 mag = runs.abs().sum(1).numpy()
                 sc = (sq * ks[b, h][j])[:, None]
-                t = (c * codes * sc).reshape(G, group, -1)
-                es = (c * 2.02 * g9 * mag * sc).reshape(G, group, -1)          # fp32 additions of both instructions
+                t = (codes * sc).reshape(G, group, -1)                          # base 2: c is in the codes of Q
+                # the first instruction starts from −m (the reference max when the tile's
+                # products are issued; 0 while it is −∞), so its fp32 additions carry |m|
+                mprev = np.where(np.isfinite(m), m, 0.0)
+                es = 2.02 * g9 * ((mag * sc).reshape(G, group, -1) + np.abs(mprev)[:, :, None])
                 t = np.where(vis, t, -np.inf)
                 es = np.where(vis, es, 0.0)
                 tmax = t.max(axis=2)
@@ -409,7 +438,9 @@ def _step_model(q, k, v, scale, causal, rows, block, round_p, mma_exact, group, 
                 # how far the kernel's log2 P̃ may lie from this one
                 mfin = np.where(np.isfinite(m), m, 0.0)[:, :, None]
                 tv = np.where(vis, t, 0.0)
-                ex = (es + es_m[:, :, None] + 4 * U_F32 * (np.abs(tv) + np.abs(mfin) + np.abs(tv - mfin))
+                # (a tile that moved the max re-offsets its exponents by mprev − m in fp32)
+                ex = (es + es_m[:, :, None]
+                      + 4 * U_F32 * (np.abs(tv) + np.abs(mfin) + np.abs(tv - mfin) + np.abs(mprev)[:, :, None])
                       + EXP2_REL / np.log(2.0) + 2.0 ** -24)
                 ex = np.where(vis, ex, 0.0)
                 exm = np.maximum(exm, ex.max(axis=2))
@@ -529,7 +560,7 @@ def fp8_step_allowance(model):
 
 
 def _logit_trunc_bound(q8, qs, k8, ks, rows, block):
-    """Schedule-free bound T [R, N] (raw logit units) on how far the matrix
+    """Schedule-free bound T [R, N] (the logits' own units: base 2) on how far the matrix
     instruction's truncation moves the logits q̂·k̂ of one (b, h): a run of 8
     products loses less than 8 grid steps 2^(E − 13), and E ≤ the run's largest
     e(q₈) plus its largest e(k₈), so T = s_q s_k·Σ_runs 2^(Eq_run + Ek_run − 10),
@@ -554,13 +585,13 @@ def fp8_mma_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=FP8_P_
     of its |products| (a power-of-two operand scale scales both alike).  Second
     product: |ΔO| ≤ 2^-10·Σ_j w_j|v̂_j| / ℓ with w_j/ℓ ≤ (1 + 2^-4)·p_j +
     2^-17·(1 + 2^-10)·P_b(j) (the rounded weight, as in fp8_allowance).  First product: logit j
-    moves by less than T_j (``_logit_trunc_bound``, times the scale), which
+    moves by less than T_j (``_logit_trunc_bound`` in base-2 units, times ln 2), which
     moves each weight by a factor within e^(±T_j): O by at most
     Σ_j p_j·(e^(2T_j) − 1)·(|v̂_j| + |O|) (numerator and ℓ), and
     L = ln Σ_j e^(s_j) by at most λ = ln Σ_j p_j e^(T_j).
     Returns (allow_O [B, H, R, d], allow_L [B, H, R]) for the query rows ``rows``."""
     from .ref import scores, safe_softmax
-    q8, qs = quantize_blocks(q, block)
+    q8, qs = quantize_blocks(prescale_q(q, scale), block)
     k8, ks = quantize_blocks(k, block)
     v8, vs = quantize_blocks(v, block)
     qh, kh, vh = (dequantize_blocks(x, s_, block) for x, s_ in ((q8, qs), (k8, ks), (v8, vs)))
@@ -570,14 +601,14 @@ def fp8_mma_allowance(q, k, v, scale, causal, block=64, rows=None, pblock=FP8_P_
     out_l = np.empty((B, H, rows.size))
     for b in range(B):
         for h in range(H):
-            s = scores(qh[b, h][rows], kh[b, h], scale, causal, rows)
+            s = scores(qh[b, h][rows], kh[b, h], LN2, causal, rows)
             p, _, l = safe_softmax(s)
             o = p @ vh[b, h]
             av = np.abs(vh[b, h])
             seen = np.isfinite(s).astype(np.float64)
             pv = 2.0 ** -10 * ((1 + 2.0 ** -4) * (p @ av)
                                + 2.0 ** -17 * (1 + 2.0 ** -10) * _block_mass(p, seen, av, pblock))
-            tb = np.where(p > 0, scale * _logit_trunc_bound(q8[b, h], qs[b, h], k8[b, h], ks[b, h], rows, block), 0.0)
+            tb = np.where(p > 0, LN2 * _logit_trunc_bound(q8[b, h], qs[b, h], k8[b, h], ks[b, h], rows, block), 0.0)
             qk = (p * np.expm1(2 * tb)) @ av + (p * np.expm1(2 * tb)).sum(axis=1)[:, None] * np.abs(o)
             out[b, h] = pv + qk
             out_l[b, h] = np.log((p * np.exp(tb)).sum(axis=1))

@@ -74,10 +74,11 @@ int main() {
   EXPECT(fa_decode_noalloc(P[0], P[1], P[2], P[3], L, 2, 4, 1000, 128, 0.1f, 7, nullptr), FA_ERR_LAUNCH);
   // FP8
   const size_t pk = fa_fp8_packed_bytes(1, 2, 300, 128);
-  EXPECT(fa_quantize_fp8(P[0], P[1], P[2], 1, 2, 300, 128, P[3], pk - 1, nullptr), FA_ERR_WORKSPACE);
-  EXPECT(fa_quantize_fp8(P[0], P[1], P[2], 1, 2, 300, 128, P[3], pk, nullptr), FA_ERR_LAUNCH);
-  EXPECT(fa_fwd_fp8(P[3], pk - 1, P[4], (float*)P[5], 1, 2, 300, 128, 0.1f, 1, nullptr), FA_ERR_WORKSPACE);
-  EXPECT(fa_fwd_fp8(P[3], pk, P[4], (float*)P[5], 1, 2, 300, 128, 0.1f, 1, nullptr), FA_ERR_LAUNCH);
+  EXPECT(fa_quantize_fp8(P[0], P[1], P[2], 1, 2, 300, 128, 0.1f, P[3], pk - 1, nullptr), FA_ERR_WORKSPACE);
+  EXPECT(fa_quantize_fp8(P[0], P[1], P[2], 1, 2, 300, 128, 0.0f, P[3], pk, nullptr), FA_ERR_VALUE);
+  EXPECT(fa_quantize_fp8(P[0], P[1], P[2], 1, 2, 300, 128, 0.1f, P[3], pk, nullptr), FA_ERR_LAUNCH);
+  EXPECT(fa_fwd_fp8(P[3], pk - 1, P[4], (float*)P[5], 1, 2, 300, 128, 1, nullptr), FA_ERR_WORKSPACE);
+  EXPECT(fa_fwd_fp8(P[3], pk, P[4], (float*)P[5], 1, 2, 300, 128, 1, nullptr), FA_ERR_LAUNCH);
   // host-only helpers
   int bm = 0, bn = 0;
   EXPECT(fa_fwd_tile_shape(128, &bm, &bn), FA_OK);

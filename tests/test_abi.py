@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     _lib()
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     assert fa.fa_status_str(0) == "ok"
     for s in range(1, 9):
         assert fa.fa_status_str(s) not in ("ok", "unknown status")
@@ -251,18 +251,18 @@ def test_python_binding_rejects_bad_tensors():
         fa.fa_fwd(q.float(), q, q)
 
 
-def _q8(q=P[0], k=P[1], v=P[2], B=1, H=2, N=300, d=128, pk=P[3], pkb=1 << 30):
+def _q8(q=P[0], k=P[1], v=P[2], B=1, H=2, N=300, d=128, scale=0.1, pk=P[3], pkb=1 << 30):
     lib = _lib()
-    lib.fa_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_size_t,
-                                                                                   ctypes.c_void_p]
-    return lib.fa_quantize_fp8(q, k, v, B, H, N, d, pk, pkb, None)
+    lib.fa_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_void_p,
+                                                                                   ctypes.c_size_t, ctypes.c_void_p]
+    return lib.fa_quantize_fp8(q, k, v, B, H, N, d, scale, pk, pkb, None)
 
 
-def _f8(pk=P[3], o=P[4], lse=P[5], B=1, H=2, N=300, d=128, scale=0.1, causal=1, pkb=1 << 30):
+def _f8(pk=P[3], o=P[4], lse=P[5], B=1, H=2, N=300, d=128, causal=1, pkb=1 << 30):
     lib = _lib()
-    lib.fa_fwd_fp8.argtypes = [ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + \
-        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-    return lib.fa_fwd_fp8(pk, pkb, o, lse, B, H, N, d, scale, causal, None)
+    lib.fa_fwd_fp8.argtypes = [ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p]
+    return lib.fa_fwd_fp8(pk, pkb, o, lse, B, H, N, d, causal, None)
 
 
 def test_fp8_packed_bytes_follow_the_documented_layout():
@@ -281,11 +281,12 @@ def test_fp8_argument_checks():
     """Every call here fails validation before any HIP call."""
     assert _q8(q=None) == 1 and _q8(pk=None) == 1
     assert _q8(N=0) == 2 and _q8(d=64) == 3
+    assert _q8(scale=0.0) == 5 and _q8(scale=float("nan")) == 5 and _q8(scale=-1.0) == 5
     assert _q8(pkb=1000) == 6
     assert _q8(v=MISALIGNED) == 4
     assert _q8(pk=P[0]) == 8  # the buffer over q
     assert _f8(pk=None) == 1 and _f8(lse=None) == 1
-    assert _f8(B=0) == 2 and _f8(d=64) == 3 and _f8(scale=0.0) == 5 and _f8(scale=float("nan")) == 5
+    assert _f8(B=0) == 2 and _f8(d=64) == 3
     assert _f8(o=MISALIGNED) == 4
     assert _f8(o=P[3]) == 8  # O over the packed operands
     assert _f8(pkb=1000) == 6  # a packed buffer smaller than the layout needs

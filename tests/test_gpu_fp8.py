@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 import exact_attention_31_amd as fa
 import synth
-from oracle.fp8 import check_fp8, e4m3_decode_table, fp8_contract, quantize_blocks
+from oracle.fp8 import check_fp8, e4m3_decode_table, fp8_contract, prescale_q, quantize_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -66,13 +66,13 @@ def test_quantize_matches_oracle_bit_for_bit(N):
     _say("[case] fp8 quantize", N)
     q, k, v = synth.make_prefill(w)
     k[0, 1, : min(N, 64)] = 0  # an all-zero block
-    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda())
+    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda(), scale=w.scale)
     torch.cuda.synchronize()
     L = _layout(B, H, N)
     assert fa.fa_fp8_packed_bytes(B, H, N, d) == L["total"]
     buf = packed.cpu().numpy()
     T = L["T"]
-    for name, x in (("q", q), ("k", k), ("v", v)):
+    for name, x in (("q", prescale_q(q, w.scale)), ("k", k), ("v", v)):  # Q carries the softmax scale in base 2
         x8, s = quantize_blocks(x, 64)
         sc = buf[L[name + "s"]:L[name + "s"] + B * H * T * 4].view(np.int32).reshape(B, H, T)
         assert np.array_equal(sc, (np.log2(s) + 127).astype(np.int32)), name
@@ -90,8 +90,8 @@ def test_quantize_matches_oracle_bit_for_bit(N):
 
 def _fwd_case(w, rows=None, heads=None):
     q, k, v = synth.make_prefill(w)
-    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda())
-    o, lse = fa.fa_fwd_fp8(packed, w.B, w.H, w.N, 128, scale=w.scale, causal=w.causal)
+    packed = fa.fa_quantize_fp8(q.cuda(), k.cuda(), v.cuda(), scale=w.scale)
+    o, lse = fa.fa_fwd_fp8(packed, w.B, w.H, w.N, 128, causal=w.causal)
     torch.cuda.synchronize()
     hs = list(range(w.H)) if heads is None else heads
     con = fp8_contract(q[:, hs], k[:, hs], v[:, hs], w.scale, w.causal, rows=rows)

@@ -64,9 +64,9 @@ def _step(t, scale, dscale, tbl, lens):
     g2 = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale=scale, causal=True)
     od, ld = fa.fa_decode(t["qd"], t["kd"], t["vd"], scale=dscale, num_splits=16)
     op, lp = fa.fa_decode_paged(t["qp"], t["kp"], t["vp"], tbl, seqlens=lens, scale=dscale, num_splits=5)
-    packed = fa.fa_quantize_fp8(t["q"], t["k"], t["v"])
+    packed = fa.fa_quantize_fp8(t["q"], t["k"], t["v"], scale=scale)
     B, H, N, d = t["q"].shape
-    o8, l8 = fa.fa_fwd_fp8(packed, B, H, N, d, scale=scale, causal=True)
+    o8, l8 = fa.fa_fwd_fp8(packed, B, H, N, d, causal=True)
     return [o, lse, *g2, od, ld, op, lp, o8, l8]
 
 

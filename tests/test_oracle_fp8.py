@@ -122,14 +122,22 @@ def _representable(rng, shape, block, scales_log2):
 
 
 def test_fp8_attention_is_exact_attention_on_representable_inputs():
+    """Inputs whose blocks are E4M3 codes times a power of two, and a scale whose
+    base-2 form c = scale·log2(e) is a power of two in fp32 (scale = ln 2 / 4:
+    fp32(ln 2 / 4)·fp32(log2 e) rounds to exactly 1/4), so that c·Q is
+    representable too: quantising changes nothing and the FP8 attention is exact
+    attention, to the last bit."""
+    from oracle.fp8 import logit_scale_f32
     rng = np.random.default_rng(11)
     shape = (1, 2, 150, 16)
     q = _representable(rng, shape, 64, [-7, -9])
     k = _representable(rng, shape, 32, [-6, -8, -7])
     v = _representable(rng, shape, 32, [-5, -9])
+    scale = LN2 / 4
+    assert logit_scale_f32(scale) == np.float32(0.25)
     for causal in (False, True):
-        o, l = attention_fp8_ref(q, k, v, 0.25, causal, q_block=64, kv_block=32)
-        ro, rl = attention_ref(q, k, v, 0.25, causal)
+        o, l = attention_fp8_ref(q, k, v, scale, causal, q_block=64, kv_block=32)
+        ro, rl = attention_ref(q, k, v, scale, causal)
         assert np.array_equal(o, ro) and np.array_equal(l, rl)
 
 
@@ -162,13 +170,13 @@ def _sim_kernel(q, k, v, scale, causal, shift, rng):
     """The FP8 forward's arithmetic on the CPU: P̃ against a reference max below
     the true one by up to `shift` (in natural-log units), block-quantised for the
     second product (_round_p_blocks), O divided by the sum of the unrounded P̃."""
-    from oracle.fp8 import dequantize_blocks, quantize_blocks
+    from oracle.fp8 import dequantize_blocks, prescale_q, quantize_blocks
     from oracle.ref import scores
-    qh, kh, vh = (dequantize_blocks(*quantize_blocks(t, 64), 64) for t in (q, k, v))
+    qh, kh, vh = (dequantize_blocks(*quantize_blocks(t, 64), 64) for t in (prescale_q(q, scale), k, v))
     o = np.empty(qh.shape)
     for b in range(qh.shape[0]):
         for h in range(qh.shape[1]):
-            s = scores(qh[b, h], kh[b, h], scale, causal)
+            s = scores(qh[b, h], kh[b, h], LN2, causal)  # base-2 logits of c·Q, in natural-log units
             m = s.max(axis=1) - rng.uniform(0, shift, s.shape[0])
             pt = np.exp(s - m[:, None])
             o[b, h] = (_round_p_blocks(pt) @ vh[b, h]) / pt.sum(axis=1)[:, None]
@@ -277,9 +285,11 @@ def test_step_model_schedule():
     """The reference max of a 32-row group moves for every row of the group when
     one row outgrows it by more than 2^48 (growths 56 and 52, E4M3-exact after
     quantisation), not at 44, and a growth within the fp32 error bound of the
-    threshold (48 exactly, nudged either way by the scale) is flagged."""
+    threshold (48 exactly) is flagged.  The scale enters through the quantised
+    codes of c·Q, so nudging it by 1e-9 either way leaves c = 1 in fp32 and the
+    growth at 48 exactly: not moved, flagged."""
     cases = [(56.0, 1.0, 2, False), (52.0, 1.0, 2, False), (44.0, 1.0, 1, False),
-             (48.0, 1.0 + 1e-9, 2, True), (48.0, 1.0 - 1e-9, 1, True), (48.0, 1.0, 1, True)]
+             (48.0, 1.0 + 1e-9, 1, True), (48.0, 1.0 - 1e-9, 1, True), (48.0, 1.0, 1, True)]
     for grow, f, moves, amb in cases:
         q, k, v = _integer_logit_inputs(300, grow_at=128, grow_row=3, grow=grow, base=4.0)
         m = fp8_step_model(q, k, v, LN2 * f, False)
@@ -384,13 +394,18 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows, flush=False):
     row's 32-key half tile divided by 2^σ (σ from the float32 sum of the half)
     and rounded to E4M3 by torch's float8_e4m3fn conversion, the second product
     by the instruction on the keys in the V tile order with each run scaled by
-    its half's 2^σ, O = acc·(1/ℓ) rounded to bf16, L = m·scale + ln ℓ.  ``flush``:
-    exp2 returns 0 for results below fp32's normal range.  Returns (O, L) on the
-    rows of every 32-row group that holds one of ``rows``."""
+    its half's 2^σ, O = acc·(1/ℓ) rounded to bf16, L = (m + log2 ℓ)·ln 2.  Q is
+    quantised as c·Q (c = scale·log2 e in fp32), so the logits are base 2; the
+    first instruction of a tile starts from −m (m when the tile's products are
+    issued, 0 while it is −∞) with the block scales applied to each run, and a
+    tile that moves m re-offsets its logits in float32.  ``flush``: exp2 returns
+    0 for results below fp32's normal range.  Returns (O, L) on the rows of
+    every 32-row group that holds one of ``rows``."""
     from oracle.fp8 import quantize_blocks
-    (q8, qs), (k8, ks), (v8, vs) = (quantize_blocks(t, 64) for t in (q, k, v))
-    B, H, N, d = q8.shape
     c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    qc = (torch.as_tensor(q).float().numpy() * c).astype(np.float32)   # c·Q, one float32 rounding
+    (q8, qs), (k8, ks), (v8, vs) = (quantize_blocks(t, 64) for t in (qc, k, v))
+    B, H, N, d = q8.shape
     order = [32 * ((j >> 4) & 1) + 8 * ((j & 15) >> 2) + 4 * (j >> 5) + (j & 3) for j in range(64)]
     run_half = [order[8 * g] // 32 for g in range(8)]  # the 32-key half tile each run of 8 slots holds
     groups = np.unique(np.asarray(rows) // 32)
@@ -407,13 +422,16 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows, flush=False):
                 m = np.full(r.size, -np.inf, np.float32)
                 ell = np.zeros(r.size, np.float32)
                 acc = torch.zeros((r.size, d), dtype=torch.float32)
+                mo = np.zeros(r.size, np.float32)      # the offset the tiles' logits start from
                 for j in range(0, N, 64):
                     kt = np.zeros((64, d), np.float32)
                     kt[:min(64, N - j)] = k8[b, h][j:j + 64]
-                    s = torch.zeros((r.size, 64), dtype=torch.float32)
+                    rs = torch.full((r.size, 8), float(np.float32(sq * np.float32(ks[b, h][j // 64]))))
+                    s = torch.from_numpy(np.repeat(-mo[:, None], 64, axis=1))
                     for half in (0, 1):
-                        s = _instr_f32(qr[:, 64 * half:64 * half + 64], f(kt[:, 64 * half:64 * half + 64].T), s)
-                    s = s.numpy() * np.float32(sq * np.float32(ks[b, h][j // 64]))
+                        s = _instr_f32(qr[:, 64 * half:64 * half + 64], f(kt[:, 64 * half:64 * half + 64].T), s,
+                                       run_scale=rs)
+                    s = s.numpy()
                     keys = j + np.arange(64)
                     dead = keys[None, :] >= N
                     if causal:
@@ -421,17 +439,20 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows, flush=False):
                     s = np.where(dead, np.float32(-np.inf), s)
                     if not np.isfinite(s).any():
                         continue
-                    mt = s.max(axis=1)
+                    mt = (s.max(axis=1) + mo).astype(np.float32)       # the tile's row max, base 2
                     with np.errstate(invalid="ignore"):
-                        grow = (mt - m) * c
+                        grow = mt - m
+                    off = np.zeros(r.size, np.float32)
                     if np.any(grow > np.float32(48.0)):
                         mn = np.fmax(m, mt)
                         with np.errstate(invalid="ignore"):
-                            al = np.exp2((m - mn) * c).astype(np.float32)
+                            al = np.exp2(m - mn).astype(np.float32)
                         al = np.where(np.isneginf(m), np.float32(0), al)
                         ell, acc, m = ell * al, acc * torch.from_numpy(al)[:, None], mn
+                        off = (mo - m).astype(np.float32)
+                        mo = m.copy()
                     with np.errstate(invalid="ignore"):
-                        x = np.exp2(s * c - (m * c)[:, None]).astype(np.float32)
+                        x = np.exp2((s + off[:, None]).astype(np.float32)).astype(np.float32)
                     x = np.where(np.isfinite(s), x, np.float32(0))
                     if flush:
                         x = np.where(x < np.float32(2.0 ** -126), np.float32(0), x)
@@ -446,7 +467,7 @@ def _sim_fp32_kernel(q, k, v, scale, causal, rows, flush=False):
                                      run_scale=torch.from_numpy(sc[:, run_half]))
                     ell = (ell + x.sum(axis=1, dtype=np.float32)).astype(np.float32)
                 o[b, h] = (acc * torch.from_numpy(np.float32(1) / ell)[:, None]).numpy()
-                lse[b, h] = m * np.float32(scale) + np.log(ell)
+                lse[b, h] = (m + np.log2(ell)) * np.float32(np.log(2.0))
         outs_o.append(o)
         outs_l.append(lse)
     o = torch.from_numpy(np.concatenate(outs_o, axis=2)).to(torch.bfloat16).double().numpy()
