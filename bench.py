@@ -454,7 +454,8 @@ def time_fp8(torch, fa, synth, dev, args):
     fa_fwd_fp8 on operands fa_quantize_fp8 wrote beforehand, interleaved with the
     bf16 fa_fwd on the same inputs, W + K calls each between HIP events; the
     quantising pass is timed on its own.  ``warm`` times K calls of each back to
-    back as well."""
+    back as well, and ``graph`` K calls of each replayed from a HIP graph (no host
+    work between the calls)."""
     res = {}
     for wname in ("llama3_8b_causal_b1h32n4096d128_kboost", "long_noncausal_b1h16n16384d128"):
         w = synth.BY_NAME[wname]
@@ -495,6 +496,20 @@ def time_fp8(torch, fa, synth, dev, args):
                 e[1].record()
             torch.cuda.synchronize()
             warm[label] = sum(e[0].elapsed_time(e[1]) for e in evw) / len(evw)
+            # and K calls captured in one HIP graph, timed as one replay (no host work between them)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    call()
+            graph.replay()
+            torch.cuda.synchronize()
+            g0, g1 = Event(), Event()
+            g0.record()
+            graph.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            warm[label + "_graph"] = g0.elapsed_time(g1) / args.steps
+            del graph
         flops = synth.prefill_flops(w)
         tf = flops / (f8 * 1e-3) / 1e12
         res[w.name] = {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(f8, 4),
@@ -502,7 +517,10 @@ def time_fp8(torch, fa, synth, dev, args):
                        "speedup_vs_bf16": round(bf / f8, 3), "quantize_ms": round(qz, 4),
                        "warm": {"ms": round(warm["fp8"], 4), "bf16_ms": round(warm["bf16"], 4),
                                 "speedup_vs_bf16": round(warm["bf16"] / warm["fp8"], 3),
-                                "note": f"{args.steps} calls of each back to back"}}
+                                "note": f"{args.steps} calls of each back to back"},
+                       "graph": {"ms": round(warm["fp8_graph"], 4), "bf16_ms": round(warm["bf16_graph"], 4),
+                                 "speedup_vs_bf16": round(warm["bf16_graph"] / warm["fp8_graph"], 3),
+                                 "note": f"{args.steps} calls of each captured in a HIP graph, timed as one replay"}}
     return res
 
 
