@@ -504,11 +504,14 @@ void fa_fwd_kernel(FwdParams p) {
   using I3 = std::integral_constant<int, 3>;
   using Y = std::true_type;
   using G = std::false_type;
-  // Tiles 0 .. n_clean-1 are seen whole by every row of the workgroup;
-  // iteration j is clean when tiles j and j+1 are.
+  // Tiles 0 .. n_clean-1 are seen whole by every row of the workgroup.
+  // Iteration j is clean when tile j is and a tile j+1 exists: that tile's
+  // first key is then at most the workgroup's first row + 1, so every
+  // wavefront sees it and computes its Sᵀ in either form.
   const int n_clean = SPARSE ? 0 : CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  const int n_clean_it = min(n_clean, n_tiles - 1);
   int j = 0;
-  for (; j + 4 <= n_clean - 1; j += 4) {
+  for (; j + 4 <= n_clean_it; j += 4) {
     iter(j, I0{}, Y{});
     iter(j + 1, I1{}, Y{});
     iter(j + 2, I2{}, Y{});

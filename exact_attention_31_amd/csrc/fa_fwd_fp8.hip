@@ -419,9 +419,12 @@ void fa_fwd_fp8_kernel(Fp8FwdParams p, const int* __restrict__ ks_all, const int
   using I3 = std::integral_constant<int, 3>;
   using Y = std::true_type;
   using G = std::false_type;
+  // iteration j is clean when tile j is whole for every row and a tile j+1
+  // exists (every wavefront then sees that tile)
   const int n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  const int n_clean_it = min(n_clean, n_tiles - 1);
   int j = 0;
-  for (; j + 4 <= n_clean - 1; j += 4) {
+  for (; j + 4 <= n_clean_it; j += 4) {
     iter(j, I0{}, Y{});
     iter(j + 1, I1{}, Y{});
     iter(j + 2, I2{}, Y{});
