@@ -104,3 +104,75 @@ def test_graph_replays_match_eager_on_new_inputs():
         names = ("o", "lse", "dq", "dk", "dv", "o_decode", "lse_decode", "o_paged", "lse_paged", "o_fp8", "lse_fp8")
         for name, a, b in zip(names, outs, want):
             assert _same(a, b), (rep, name)
+
+
+def _more_inputs(seed):
+    """The prefill batch of _inputs with a seeded block mask, a grouped-query
+    decode batch (B2, Hq 8 over Hkv 2, Lmax 700 d128) and the decode batch."""
+    t, scale, dscale = _inputs(seed)
+    g = torch.Generator().manual_seed(1000 + seed)
+    t["qg"] = torch.randn(2, 8, 1, 128, generator=g).to(torch.bfloat16)
+    t["kg"] = torch.randn(2, 2, 700, 128, generator=g).to(torch.bfloat16)
+    t["vg"] = torch.randn(2, 2, 700, 128, generator=g).to(torch.bfloat16)
+    return t, scale, dscale
+
+
+def _more_step(t, scale, dscale, mask, glens):
+    """The entry points _step leaves out: block-sparse forward and backward, the
+    atomic backward, grouped-query decode with per-sequence lengths, and decode
+    into caller-owned outputs with the library's own scratch."""
+    o, lse = fa.fa_fwd_block_sparse(t["q"], t["k"], t["v"], mask, scale=scale, causal=True)
+    gs = fa.fa_bwd_block_sparse(t["q"], t["k"], t["v"], o, lse, t["do"], mask, scale=scale, causal=True)
+    od, ld = fa.fa_fwd(t["q"], t["k"], t["v"], scale=scale, causal=True)
+    ga = fa.fa_bwd_atomic(t["q"], t["k"], t["v"], od, ld, t["do"], scale=scale, causal=True)
+    og, lg = fa.fa_decode_gqa(t["qg"], t["kg"], t["vg"], seqlens=glens, scale=dscale, num_splits=4)
+    on = torch.empty(t["qd"].shape, dtype=torch.bfloat16, device=t["qd"].device)
+    ln = torch.empty(t["qd"].shape[:2], dtype=torch.float32, device=t["qd"].device)
+    fa.fa_decode_noalloc(t["qd"], t["kd"], t["vd"], on, ln, scale=dscale, num_splits=16)
+    return [o, lse, *gs, *ga, og, lg, on, ln]
+
+
+def test_graph_replays_more_entry_points():
+    """The same replay protocol over the remaining entry points.  The atomic
+    backward adds its dQ shares in no fixed order, so its dQ is compared within
+    one bf16 step of its largest value; every other output bit for bit."""
+    dev = "cuda"
+    first, scale, dscale = _more_inputs(0)
+    static = {n: x.to(dev) for n, x in first.items()}
+    w = W[2].with_(B=1, H=4, N=1000, d=128, causal=True)
+    mask = synth.make_block_mask(w, 0.4).to(dev)
+    glens = torch.tensor([700, 523], dtype=torch.int32, device=dev)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _more_step(static, scale, dscale, mask, glens)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = _more_step(static, scale, dscale, mask, glens)
+    torch.cuda.synchronize()
+
+    names = ("o_sparse", "lse_sparse", "dq_sparse", "dk_sparse", "dv_sparse", "dq_atomic", "dk_atomic",
+             "dv_atomic", "o_gqa", "lse_gqa", "o_noalloc", "lse_noalloc")
+    for rep in range(3):
+        _say("[case] graph replay, more entry points", rep)
+        fresh, _, _ = _more_inputs(rep)
+        for n, x in fresh.items():
+            static[n].copy_(x.to(dev))
+        want = [x.clone() for x in _more_step(static, scale, dscale, mask, glens)]
+        torch.cuda.synchronize()
+        for x in outs:
+            x.fill_(float("nan") if x.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, outs, want):
+            if name == "dq_atomic":
+                top = b.float().abs().max().item()
+                err = (a.float() - b.float()).abs().max().item()
+                assert err <= top * 2.0**-7, (rep, name, err, top)
+            else:
+                assert _same(a, b), (rep, name)
