@@ -507,8 +507,19 @@ void fa_fwd_kernel(FwdParams p) {
   // Tiles 0 .. n_clean-1 are seen whole by every row of the workgroup.
   // Iteration j is clean when tile j is and a tile j+1 exists: that tile's
   // first key is then at most the workgroup's first row + 1, so every
-  // wavefront sees it and computes its Sᵀ in either form.
-  const int n_clean = SPARSE ? 0 : CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  // wavefront sees it and computes its Sᵀ in either form.  SPARSE: with N a
+  // multiple of the mask block every kept tile is whole, and every row sees all
+  // of its keys when non-causal, those of the blocks before its own when causal
+  // (the list is in key order, so only its last block can be the query block's
+  // own); a wavefront that does not see tile j+1 computes its Sᵀ for nothing.
+  int n_clean;
+  if constexpr (SPARSE) {
+    const int nb = n_tiles >> 1;
+    const int own_last = nb > 0 ? __builtin_amdgcn_readfirstlane((int)kblocks[nb - 1]) == qb : 0;
+    n_clean = N % kSparseBlock != 0 ? 0 : !CAUSAL ? n_tiles : 2 * (nb - own_last);
+  } else {
+    n_clean = CAUSAL ? min(N / T::BN, (q0 + 1) / T::BN) : N / T::BN;
+  }
   const int n_clean_it = min(n_clean, n_tiles - 1);
   int j = 0;
   for (; j + 4 <= n_clean_it; j += 4) {
